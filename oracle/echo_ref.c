@@ -1,0 +1,518 @@
+/*
+ * echo_ref.c — the CPU oracle for Echo's error-compensated low-bit all-reduce.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file defines what the GPU library must
+ * compute; it is plain, slow, single-threaded C with no blocking or fusion.
+ * Only the test-suite, the smoke check and the benchmark's CPU-baseline leg
+ * load it.  It shares no source, header, table or helper with the HIP
+ * library, and it includes nothing from it.
+ *
+ * Sources (the method is described, not listed, on these pages):
+ *   [EchoCard]  "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication
+ *               for LLM Training and Inference" (arXiv 2610.14277), paper card:
+ *               abstract, Fig. 1, Fig. 2(a)/(b), Table 8, appendix Fig. 4.
+ *   [Blog]      "Your All-Reduce Is 4x Overpriced: Echo's 4-Bit Error-Feedback
+ *               Trick for Tensor-Parallel Training", sections "The cancellation
+ *               rule" and "The part of your stack nobody profiles".
+ *
+ * Arithmetic.  The pages say only "high precision" for the owner's sum; the
+ * parity bar this oracle serves fixes it as IEEE fp32, summed in rank order
+ * j = 0..P-1 with no fused multiply-add.  Build with
+ * -O2 -ffp-contract=off -fno-fast-math so that every float operation below is
+ * one correctly rounded IEEE operation (x86-64 SSE, round to nearest even).
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the design notes):
+ *   - the quantizer ("zero-aware asymmetric", [EchoCard] Table 8; Eqn. (8) is
+ *     named in Fig. 4 but not printed) is the min/max affine quantizer whose
+ *     range is widened to contain 0, with an integer zero point so that 0 is
+ *     a grid point; its scale and zero point are stored as IEEE binary16
+ *     ([Blog], "4-bit integers with half-precision parameters per group");
+ *   - codes are unsigned in [0, 2^b-1]; for b = 4 two codes share a byte,
+ *     the even element in the low nibble;
+ *   - segment s (P equal contiguous segments) is owned by rank s;
+ *   - the owner's own term is compensated but never quantized before the sum;
+ *   - the two-timescale compensator is an error debt: a fraction alpha of the
+ *     newest error is returned at the next call, the rest enters a slow
+ *     memory M that is released at rate beta per call.
+ *
+ * Parity status of each function is stated at its definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define REF_OK 0
+#define REF_EINVAL (-1)
+#define REF_EUNSUP (-3)
+#define REF_ESHAPE (-4)
+
+#define REF_ERR_NEGATED 1   /* write -e (the next call's compensation) instead of e */
+#define REF_OUT_F32 0
+#define REF_OUT_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Number formats, from the IEEE 754 definitions.                            */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* binary32 -> binary16, round to nearest, ties to even, subnormals kept.
+ * Written from the format definition: the input is an integer significand M
+ * times 2^(e-23); the output grid at the input's binade has quantum
+ * 2^(max(e,-14)-10); drop the bits below that quantum with a
+ * round-half-even decision, and let a carry roll into the exponent field.
+ * Pinned against numpy's float16 conversion on every binade boundary and
+ * rounding pattern (and exhaustively in the slow suite). */
+uint16_t echo_ref_f32_to_f16(float f)
+{
+    uint32_t u = f32_bits(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);      /* NaN  */
+    if (a == 0x7F800000u) return (uint16_t)(sign | 0x7C00u);     /* inf  */
+    if (a < 0x00800000u) return sign;  /* binary32 subnormal: below 2^-126, far under half of 2^-24 */
+    int e = (int)(a >> 23) - 127;                  /* unbiased exponent     */
+    uint32_t M = (a & 0x007FFFFFu) | 0x00800000u;  /* 24-bit significand    */
+    if (e > 15) return (uint16_t)(sign | 0x7C00u); /* >= 2^16: overflow     */
+    if (e < -25) return sign;                      /* < 2^-25: rounds to 0  */
+    int shift = 13 + (e < -14 ? (-14 - e) : 0);    /* 13 .. 24              */
+    uint32_t N = M >> shift;
+    uint32_t rem = M & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (N & 1u))) N += 1u;
+    if (e < -14)               /* subnormal result; N == 1024 is the smallest normal */
+        return (uint16_t)(sign | N);
+    /* normal result: N in [1024, 2048]; a carry to 2048 bumps the exponent,
+     * and exponent field 31 is infinity */
+    uint32_t h = ((uint32_t)(e + 15) << 10) + (N - 1024u);
+    if (h >= 0x7C00u) h = 0x7C00u;
+    return (uint16_t)(sign | h);
+}
+
+/* binary16 -> binary32 (exact). */
+float echo_ref_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (h & 0x8000u) ? 1u : 0u;
+    uint32_t E = (h >> 10) & 0x1Fu;
+    uint32_t m = h & 0x3FFu;
+    float mag;
+    if (E == 0) mag = ldexpf((float)m, -24);
+    else if (E == 31) mag = m ? NAN : INFINITY;
+    else mag = ldexpf((float)(1024u + m), (int)E - 25);
+    return sign ? -mag : mag;
+}
+
+void echo_ref_f32_to_f16_array(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = echo_ref_f32_to_f16(in[i]);
+}
+
+/* bfloat16 is the upper half of a binary32. */
+float echo_ref_bf16_to_f32(uint16_t b) { return bits_f32((uint32_t)b << 16); }
+
+/* binary32 -> bfloat16, round to nearest, ties to even (drop 16 bits). */
+uint16_t echo_ref_f32_to_bf16(float f)
+{
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t up = u >> 16, rem = u & 0xFFFFu;
+    if (rem > 0x8000u || (rem == 0x8000u && (up & 1u))) up += 1u;
+    return (uint16_t)up;
+}
+
+void echo_ref_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = echo_ref_f32_to_bf16(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1: the zero-aware asymmetric group quantizer Q_b and its dequantizer.     */
+/* [EchoCard] Table 8 (full method: zero-aware asymmetric, g = 128); Fig. 4   */
+/* (Eqn. (8) with b = 4); [Blog] "The cancellation rule" (fp16 parameters).   */
+/* ------------------------------------------------------------------------ */
+
+/* Quantize one group of g values to unsigned b-bit codes (one per byte in q).
+ * Steps:
+ *   1. lo = min(0, min v), hi = max(0, max v): the range always holds 0.
+ *   2. hi == lo means an all-zero group: scale +0, zero point 0, codes 0.
+ *   3. s32 = (hi - lo) / Qm, Qm = 2^b - 1 (true fp32 division).
+ *   4. s = binary16(s32); a zero result becomes 2^-24, an infinite one 65504.
+ *   5. inv = 1 / s in fp32 (correctly rounded).
+ *   6. z = clamp(rint(-lo * inv), 0, Qm): an integer, so 0 sits on the grid.
+ *   7. q_i = clamp(rint(v_i * inv) + z, 0, Qm): the integer zero point is
+ *      added after rounding (rint = round half to even).
+ *   8. z is stored as binary16 (exact: an integer <= 255).
+ * Pinned by: brute-force argmin over all codes on tiny groups, exact-rational
+ * scale choice, the grid round-trip, zero-awareness and the element bound. */
+int echo_ref_quantize_group(const float* v, int g, int bits, uint8_t* q,
+                            uint16_t* scale_h, uint16_t* zero_h)
+{
+    if (bits != 4 && bits != 8) return REF_EUNSUP;
+    if (g < 1) return REF_EINVAL;
+    const int Qm = (1 << bits) - 1;
+    float lo = 0.0f, hi = 0.0f;
+    for (int i = 0; i < g; ++i) {
+        if (v[i] < lo) lo = v[i];
+        if (v[i] > hi) hi = v[i];
+    }
+    if (hi == lo) {
+        for (int i = 0; i < g; ++i) q[i] = 0;
+        *scale_h = 0;
+        *zero_h = 0;
+        return REF_OK;
+    }
+    float s32 = (hi - lo) / (float)Qm;
+    uint16_t sh = echo_ref_f32_to_f16(s32);
+    if (sh == 0x0000u) sh = 0x0001u;        /* underflow -> 2^-24 */
+    else if (sh == 0x7C00u) sh = 0x7BFFu;   /* overflow  -> 65504 */
+    float s = echo_ref_f16_to_f32(sh);
+    float inv = 1.0f / s;
+    double zr = (double)rintf(-lo * inv);
+    int z = zr < 0.0 ? 0 : (zr > (double)Qm ? Qm : (int)zr);
+    for (int i = 0; i < g; ++i) {
+        double t = (double)rintf(v[i] * inv) + (double)z;
+        q[i] = (uint8_t)(t < 0.0 ? 0 : (t > (double)Qm ? Qm : (int)t));
+    }
+    *scale_h = sh;
+    *zero_h = echo_ref_f32_to_f16((float)z);
+    return REF_OK;
+}
+
+/* Dequantizer: v_hat = (q - z) * s.  Exact in fp32: |q - z| <= 255 needs 8
+ * bits and s has an 11-bit significand, so the product fits in 24 bits. */
+float echo_ref_dequant(int q, uint16_t scale_h, uint16_t zero_h)
+{
+    int z = (int)echo_ref_f16_to_f32(zero_h);
+    return (float)(q - z) * echo_ref_f16_to_f32(scale_h);
+}
+
+/* Packed code stream: b = 4 -> element i in byte i/2, low nibble when i is
+ * even; b = 8 -> one byte per element. */
+static int code_at(const uint8_t* codes, int64_t i, int bits)
+{
+    if (bits == 8) return codes[i];
+    uint8_t byte = codes[i >> 1];
+    return (i & 1) ? (byte >> 4) : (byte & 0x0F);
+}
+
+static void code_put(uint8_t* codes, int64_t i, int bits, int q)
+{
+    if (bits == 8) { codes[i] = (uint8_t)q; return; }
+    uint8_t* byte = &codes[i >> 1];
+    if (i & 1) *byte = (uint8_t)((*byte & 0x0F) | (q << 4));
+    else       *byte = (uint8_t)((*byte & 0xF0) | q);
+}
+
+/* Per-group parameter words: params[2*k] = scale bits, params[2*k+1] = zero
+ * bits, for the group starting at message element k*g. */
+
+/* Quantize the g values u[0..g) of the group that starts at message element
+ * `base` into the code stream and the parameter array; count, if not NULL,
+ * is incremented for every element passed through the quantizer. */
+static void quantize_into(const float* u, int64_t base, int g, int bits,
+                          uint8_t* codes, uint16_t* params, uint8_t* qscratch, int* count)
+{
+    uint16_t sh, zh;
+    echo_ref_quantize_group(u, g, bits, qscratch, &sh, &zh);
+    for (int i = 0; i < g; ++i) code_put(codes, base + i, bits, qscratch[i]);
+    params[2 * (base / g)] = sh;
+    params[2 * (base / g) + 1] = zh;
+    if (count)
+        for (int i = 0; i < g; ++i) count[base + i] += 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Argument checks shared by the call-level functions below.                */
+/* ------------------------------------------------------------------------ */
+
+static int check_shape(int64_t n, int P, int64_t tile_begin, int64_t tile_len,
+                       int bits, int g)
+{
+    if (bits != 4 && bits != 8) return REF_EUNSUP;
+    if (g < 1 || (bits == 4 && (g & 1))) return REF_EUNSUP;
+    if (P < 1 || P > 64) return REF_EINVAL;
+    if (n < 0 || tile_begin < 0 || tile_len < 0) return REF_ESHAPE;
+    if (n % ((int64_t)P * g) != 0) return REF_ESHAPE;
+    int64_t S = n / P;
+    if (tile_begin % g || tile_len % g || tile_begin + tile_len > S) return REF_ESHAPE;
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2: entry pass + push quantize, for one rank.                             */
+/* [EchoCard] Fig. 2(a) (each rank quantizes the segments it does not own);  */
+/* Fig. 4 (three quantized copies, own copy kept); [Blog] "The cancellation  */
+/* rule" (compensation fused into the entry pass).                           */
+/* For every segment s != rank and every group of the tile [tile_begin,      */
+/* tile_begin + tile_len) inside it: u = f32(x) + comp (u = f32(x) when comp */
+/* is NULL); codes and parameters of Q_b(u); err = Q_hat(u) - u.             */
+/* err may alias comp: each group's compensation is read before any of its  */
+/* errors is written.                                                        */
+/* ------------------------------------------------------------------------ */
+static int push_impl(const uint16_t* x, const float* comp, int64_t n, int P, int rank,
+                     int64_t tile_begin, int64_t tile_len, int bits, int g,
+                     uint8_t* codes, uint16_t* params, float* err, int flags, int* count)
+{
+    int rc = check_shape(n, P, tile_begin, tile_len, bits, g);
+    if (rc) return rc;
+    if (rank < 0 || rank >= P) return REF_EINVAL;
+    if ((!x || !codes || !params) && n > 0) return REF_EINVAL;
+    int64_t S = n / P;
+    float* u = (float*)malloc(sizeof(float) * (size_t)g);
+    uint8_t* qs = (uint8_t*)malloc((size_t)g);
+    for (int s = 0; s < P; ++s) {
+        if (s == rank) continue;
+        for (int64_t off = 0; off < tile_len; off += g) {
+            int64_t base = (int64_t)s * S + tile_begin + off;
+            for (int i = 0; i < g; ++i) {
+                float xv = echo_ref_bf16_to_f32(x[base + i]);
+                u[i] = comp ? xv + comp[base + i] : xv;
+            }
+            quantize_into(u, base, g, bits, codes, params, qs, count);
+            if (err) {
+                uint16_t sh = params[2 * (base / g)], zh = params[2 * (base / g) + 1];
+                for (int i = 0; i < g; ++i) {
+                    float e = echo_ref_dequant(qs[i], sh, zh) - u[i];
+                    err[base + i] = (flags & REF_ERR_NEGATED) ? -e : e;
+                }
+            }
+        }
+    }
+    free(u); free(qs);
+    return REF_OK;
+}
+
+int echo_ref_quantize_ef(const uint16_t* x, const float* comp, int64_t n, int P, int rank,
+                         int64_t tile_begin, int64_t tile_len, int bits, int g,
+                         uint8_t* codes, uint16_t* params, float* err, int flags)
+{
+    return push_impl(x, comp, n, P, rank, tile_begin, tile_len, bits, g, codes, params,
+                     err, flags, NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3: owner reduce, for one owner.                                          */
+/* [EchoCard] Fig. 2(a) (dequantize the received codes, add the own          */
+/* unquantized segment in high precision, quantize the sum once for the      */
+/* all-gather); Fig. 4 (four copies, three dequantized); abstract (the sum   */
+/* reveals the injected error); [Blog] "The cancellation rule".              */
+/* For every group of the owner's segment inside the tile:                   */
+/*   t_j = u_owner (= f32(x) + comp) when j == owner, else Q_hat(codes_j);   */
+/*   acc = t_0, then acc = acc + t_j for j = 1 .. P-1 (fp32, rank order);    */
+/*   sum codes/params = Q_b(acc), written at the segment's message offset;   */
+/*   own_err = Q_hat(acc) - acc (the owner's share of the injected error).   */
+/* peer_codes[owner] and peer_params[owner] are not read.                    */
+/* ------------------------------------------------------------------------ */
+static int reduce_impl(const uint16_t* own_x, const float* own_comp,
+                       const uint8_t* const* peer_codes, const uint16_t* const* peer_params,
+                       int P, int owner, int64_t n, int64_t tile_begin, int64_t tile_len,
+                       int bits, int g, uint8_t* sum_codes, uint16_t* sum_params,
+                       float* own_err, int flags, int* count)
+{
+    int rc = check_shape(n, P, tile_begin, tile_len, bits, g);
+    if (rc) return rc;
+    if (owner < 0 || owner >= P) return REF_EINVAL;
+    if ((!own_x || !sum_codes || !sum_params || !peer_codes || !peer_params) && n > 0) return REF_EINVAL;
+    for (int j = 0; j < P; ++j)
+        if (j != owner && n > 0 && (!peer_codes[j] || !peer_params[j])) return REF_EINVAL;
+    int64_t S = n / P;
+    float* acc = (float*)malloc(sizeof(float) * (size_t)g);
+    uint8_t* qs = (uint8_t*)malloc((size_t)g);
+    for (int64_t off = 0; off < tile_len; off += g) {
+        int64_t base = (int64_t)owner * S + tile_begin + off;
+        int64_t grp = base / g;
+        for (int i = 0; i < g; ++i) {
+            float sum = 0.0f;
+            for (int j = 0; j < P; ++j) {
+                float t;
+                if (j == owner) {
+                    float xv = echo_ref_bf16_to_f32(own_x[base + i]);
+                    t = own_comp ? xv + own_comp[base + i] : xv;
+                } else {
+                    t = echo_ref_dequant(code_at(peer_codes[j], base + i, bits),
+                                         peer_params[j][2 * grp], peer_params[j][2 * grp + 1]);
+                }
+                sum = (j == 0) ? t : sum + t;
+            }
+            acc[i] = sum;
+        }
+        quantize_into(acc, base, g, bits, sum_codes, sum_params, qs, count);
+        if (own_err) {
+            uint16_t sh = sum_params[2 * grp], zh = sum_params[2 * grp + 1];
+            for (int i = 0; i < g; ++i) {
+                float e = echo_ref_dequant(qs[i], sh, zh) - acc[i];
+                own_err[base + i] = (flags & REF_ERR_NEGATED) ? -e : e;
+            }
+        }
+    }
+    free(acc); free(qs);
+    return REF_OK;
+}
+
+int echo_ref_reduce_segment(const uint16_t* own_x, const float* own_comp,
+                            const uint8_t* const* peer_codes, const uint16_t* const* peer_params,
+                            int P, int owner, int64_t n, int64_t tile_begin, int64_t tile_len,
+                            int bits, int g, uint8_t* sum_codes, uint16_t* sum_params,
+                            float* own_err, int flags)
+{
+    return reduce_impl(own_x, own_comp, peer_codes, peer_params, P, owner, n, tile_begin,
+                       tile_len, bits, g, sum_codes, sum_params, own_err, flags, NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4: quantized all-gather and tail decode, for one rank.                   */
+/* [EchoCard] Fig. 2(a) (every rank, the owner included, decodes the same    */
+/* code); Fig. 4 (every GPU holds the same values).                          */
+/* For every segment and every element of the tile inside it:               */
+/*   out[i] = Q_hat(sum codes)[i], as fp32 or as bfloat16 (nearest even).    */
+/* ------------------------------------------------------------------------ */
+int echo_ref_gather_dequant(const uint8_t* sum_codes, const uint16_t* sum_params, int64_t n,
+                            int64_t tile_begin, int64_t tile_len, int P, int bits, int g,
+                            void* out, int out_dtype)
+{
+    int rc = check_shape(n, P, tile_begin, tile_len, bits, g);
+    if (rc) return rc;
+    if (out_dtype != REF_OUT_F32 && out_dtype != REF_OUT_BF16) return REF_EUNSUP;
+    if ((!sum_codes || !sum_params || !out) && n > 0) return REF_EINVAL;
+    int64_t S = n / P;
+    for (int s = 0; s < P; ++s) {
+        for (int64_t off = 0; off < tile_len; ++off) {
+            int64_t i = (int64_t)s * S + tile_begin + off;
+            int64_t grp = i / g;
+            float v = echo_ref_dequant(code_at(sum_codes, i, bits),
+                                       sum_params[2 * grp], sum_params[2 * grp + 1]);
+            if (out_dtype == REF_OUT_F32) ((float*)out)[i] = v;
+            else ((uint16_t*)out)[i] = echo_ref_f32_to_bf16(v);
+        }
+    }
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5: the two-timescale compensator update.                                 */
+/* [EchoCard] abstract (revealed errors are fed back into later calls so old */
+/* errors cancel); [Blog] "The cancellation rule" (a two-timescale           */
+/* compensator; each error comes back at the calls that follow).             */
+/* The pages give no equation; the reading is an error debt with a fast      */
+/* fraction alpha and a slow memory M released at rate beta:                 */
+/*   c' = -(alpha*e + beta*M)          (the next call's compensation)        */
+/*   M' = (1-beta)*M + (1-alpha)*e                                            */
+/* Each product is rounded, then the sum, then negated.  With slow == NULL   */
+/* (beta == 0) the update is c' = -(alpha*e); alpha == 1 then gives classic  */
+/* error feedback, c' = -e.  comp_next may alias err; slow is updated in     */
+/* place.  Parity of the constants is unpinned (the pages print none); the   */
+/* debt identity (accumulated error == sum of M - c) pins the form.           */
+/* ------------------------------------------------------------------------ */
+int echo_ref_compensate(const float* err, float* comp_next, float* slow, int64_t n,
+                        float alpha, float beta)
+{
+    if (n < 0) return REF_ESHAPE;
+    if (!(alpha > 0.0f && alpha <= 1.0f) || !(beta >= 0.0f && beta <= 1.0f)) return REF_EINVAL;
+    if (!slow && beta != 0.0f) return REF_EINVAL;
+    if (slow && beta == 0.0f && alpha < 1.0f) return REF_EINVAL;
+    if (alpha < 1.0f && beta == 0.0f) return REF_EINVAL;
+    if ((!err || !comp_next) && n > 0) return REF_EINVAL;
+    float oma = 1.0f - alpha, omb = 1.0f - beta;
+    for (int64_t i = 0; i < n; ++i) {
+        float e = err[i];
+        if (slow) {
+            float M = slow[i];
+            float a = alpha * e;
+            float b = beta * M;
+            comp_next[i] = -(a + b);
+            float m1 = omb * M;
+            float m2 = oma * e;
+            slow[i] = m1 + m2;
+        } else {
+            float a = alpha * e;
+            comp_next[i] = -a;
+        }
+    }
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One whole all-reduce call over P ranks held in host memory: push for     */
+/* every rank, reduce for every owner, decode for every rank, then the      */
+/* compensator.  ef = 0: no compensation (comp/err/slow ignored).            */
+/* ef = 1: u = x + comp; if err is NULL the update must be classic           */
+/* (alpha = 1, beta = 0) and -e is written straight into comp (identical to  */
+/* computing e and then c' = -(1*e)); otherwise e goes to err and            */
+/* echo_ref_compensate turns it into comp (and slow).                        */
+/* Instrumentation ([EchoCard] abstract and Fig. 2: at most two              */
+/* quantizations per element per call), filled from counters that the push  */
+/* and reduce loops above increment as they run:                             */
+/*   qdepth[i] (optional, n ints): the largest number of quantizer            */
+/*     applications on any path from an input element into output i, i.e.    */
+/*     max_j (push count of rank j at i) + (sum-quantization count at i);     */
+/*   qwork[r] (optional, P int64): elements rank r passed through the         */
+/*     quantizer (its pushes plus its owner requantization).                  */
+/* ------------------------------------------------------------------------ */
+int echo_ref_allreduce(int P, int64_t n, int bits, int g, int ef, float alpha, float beta,
+                       const uint16_t* const* x, float* const* comp, float* const* slow,
+                       float* const* err, void* const* out, int out_dtype,
+                       int* qdepth, int64_t* qwork)
+{
+    int rc = check_shape(n, P, 0, 0, bits, g);
+    if (rc) return rc;
+    if (out_dtype != REF_OUT_F32 && out_dtype != REF_OUT_BF16) return REF_EUNSUP;
+    int64_t S = n / P;
+    int fused = ef && !err;
+    if (ef && fused && !(alpha == 1.0f && beta == 0.0f)) return REF_EINVAL;
+    if (ef && !comp) return REF_EINVAL;
+    int counting = qdepth || qwork;
+    size_t cbytes = bits == 4 ? (size_t)(n / 2) : (size_t)n;
+    size_t pwords = 2 * (size_t)(n / g);
+    size_t nc = counting ? (size_t)n : 0;
+    uint8_t** pc = (uint8_t**)calloc((size_t)P, sizeof(uint8_t*));
+    uint16_t** pp = (uint16_t**)calloc((size_t)P, sizeof(uint16_t*));
+    int** pushcnt = (int**)calloc((size_t)P, sizeof(int*));
+    for (int r = 0; r < P; ++r) {
+        pc[r] = (uint8_t*)calloc(cbytes + 1, 1);
+        pp[r] = (uint16_t*)calloc(pwords + 1, sizeof(uint16_t));
+        pushcnt[r] = counting ? (int*)calloc(nc + 1, sizeof(int)) : NULL;
+    }
+    uint8_t* sc = (uint8_t*)calloc(cbytes + 1, 1);
+    uint16_t* sp = (uint16_t*)calloc(pwords + 1, sizeof(uint16_t));
+    int* sumcnt = counting ? (int*)calloc(nc + 1, sizeof(int)) : NULL;
+    int flags = fused ? REF_ERR_NEGATED : 0;
+
+    for (int r = 0; r < P && !rc; ++r) {
+        float* c = ef ? comp[r] : NULL;
+        float* e = ef ? (fused ? comp[r] : err[r]) : NULL;
+        rc = push_impl(x[r], c, n, P, r, 0, S, bits, g, pc[r], pp[r], e, flags, pushcnt[r]);
+    }
+    for (int o = 0; o < P && !rc; ++o) {
+        float* c = ef ? comp[o] : NULL;
+        float* e = ef ? (fused ? comp[o] : err[o]) : NULL;
+        rc = reduce_impl(x[o], c, (const uint8_t* const*)pc, (const uint16_t* const*)pp,
+                         P, o, n, 0, S, bits, g, sc, sp, e, flags, sumcnt);
+    }
+    for (int r = 0; r < P && !rc; ++r)
+        rc = echo_ref_gather_dequant(sc, sp, n, 0, S, P, bits, g, out[r], out_dtype);
+    if (ef && !fused)
+        for (int r = 0; r < P && !rc; ++r)
+            rc = echo_ref_compensate(err[r], comp[r], slow ? slow[r] : NULL, n, alpha, beta);
+    if (!rc && qdepth) {
+        for (int64_t i = 0; i < n; ++i) {
+            int deepest = 0;
+            for (int j = 0; j < P; ++j)
+                if (pushcnt[j][i] > deepest) deepest = pushcnt[j][i];
+            qdepth[i] = deepest + sumcnt[i];
+        }
+    }
+    if (!rc && qwork) {
+        for (int r = 0; r < P; ++r) {
+            int64_t w = 0;
+            for (int64_t i = 0; i < n; ++i) w += pushcnt[r][i];
+            for (int64_t i = (int64_t)r * S; i < (int64_t)(r + 1) * S; ++i) w += sumcnt[i];
+            qwork[r] = w;
+        }
+    }
+    for (int r = 0; r < P; ++r) { free(pc[r]); free(pp[r]); free(pushcnt[r]); }
+    free(pc); free(pp); free(pushcnt); free(sc); free(sp); free(sumcnt);
+    return rc;
+}
