@@ -1,0 +1,248 @@
+"""Benchmark: one simulated Echo all-reduce call on one MI355X, 1 GiB messages.
+
+A step is one echo_allreduce_sim call over P simulated ranks: push quantize
+with the compensation added in the entry pass, owner reduce, tail decode, and
+the compensator update (classic error feedback: -e written in place), with
+tiles staggered across four HIP streams.  Inputs: 2^29 bfloat16 elements per
+rank, Laplace(0, 1), resident in HBM before timing starts.
+
+value = algorithmic bytes of the call / time, in GB/s (10^9 B/s), where the
+algorithmic bytes per message element per rank are
+    B = 2 + o + 8*ef + k_b * (3 - 1/P),  k_b = b/8 + 4/128
+(bf16 in, output o bytes, compensation read + write, codes and per-group
+parameters written by the push, read by the owner, written once by the
+owner, read by every rank's tail).  Each simulated rank does its own reads.
+
+Also printed (same JSON line):
+  roofline      the dominant kernel (push quantize): algorithmic bytes per
+                launch / its mean launch time from HIP events on its stream,
+                against 8 TB/s; traffic from the committed rocprofv3 counter
+                summary if it was taken on the current kernel source.
+  cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same
+                workload: 1/32 of every segment's groups, same byte formula.
+  p8            the same measurement at P = 8.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+G = 128
+N_1GIB = 1 << 29
+METRIC = "fused quant/reduce/gather GB/s and % of HBM peak per call, 1 GB msg, P=4/8"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("echo_kernels.hpp", "echo_api.hip"):
+        with open(os.path.join(ROOT, "error_feedback_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_elem(P, bits, ef, out_bytes):
+    kb = bits / 8 + 4 / G
+    return 2 + out_bytes + (8 if ef else 0) + kb * (3 - 1 / P)
+
+
+def push_bytes_per_elem(bits, ef):
+    return 2 + (8 if ef else 0) + bits / 8 + 4 / G
+
+
+def committed_traffic(P, tiles, n):
+    """HBM traffic per push launch from profiles/push_quantize_onegb_counters.json,
+    if those counters were taken on the current kernel source and shape."""
+    path = os.path.join(ROOT, "profiles", "push_quantize_onegb_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        key = f"P{P}_tiles{tiles}_n{n}"
+        if d.get("kernel_source_hash") != kernel_source_hash() or key not in d.get("push", {}):
+            return None
+        return d["push"][key]["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, out_bf16, ef):
+    dev = "cuda:0"
+    xs = [inputs.laplace(r, n, device=dev) for r in range(P)]
+    comps = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if ef else None
+    odt = torch.int16 if out_bf16 else torch.float32
+    outs = [torch.empty(n, dtype=odt, device=dev) for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=dev)
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+    args = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=tiles,
+                              out_dtype=echo.OUT_BF16 if out_bf16 else echo.OUT_F32, ef=ef, comps=comps)
+    for _ in range(warmup):
+        echo.echo_allreduce_sim(args, streams=streams)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(main)
+    for _ in range(steps):
+        echo.echo_allreduce_sim(args, streams=streams)
+    ev1.record(main)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(wall * 1e3, ev_ms) / steps
+
+    B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4)
+    value = P * n * B / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the push of one rank over one tile, timed with events on
+    # the stream it is launched on (the sim launches the same kernel, same size)
+    S = n // P
+    gps = S // G
+    tile_groups = -(-gps // min(tiles, gps))
+    tile_len = tile_groups * G
+    reps = max(8, 2 * P)
+    # codes and params of this timing go to the workspace's first rank slots
+    cb = n // 2 if bits == 4 else n
+    codes_t, params_t = ws, ws[((cb + 255) // 256) * 256 * P:]
+
+    def push(r):
+        echo.echo_quantize_ef(xs[r], comps[r] if ef else None, n, P, r, 0, tile_len, bits, G,
+                              codes_t, params_t, comps[r] if ef else None,
+                              echo.ERR_NEGATED if ef else 0, stream=main)
+
+    for r in range(P):     # warm
+        push(r)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for i in range(reps):
+        push(i % P)
+    e1.record(main)
+    torch.cuda.synchronize()
+    push_ms = e0.elapsed_time(e1) / reps
+    push_bytes = (P - 1) * tile_len * push_bytes_per_elem(bits, ef)
+    achieved = push_bytes / (push_ms * 1e-3) / 1e9
+    traffic = committed_traffic(P, tiles, n)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "push_kernel<4,2> (echo_quantize_ef)", "launch_elements": (P - 1) * tile_len,
+            "algorithmic_bytes_per_launch": int(push_bytes), "mean_launch_ms": round(push_ms, 4)}
+    del xs, comps, outs, ws
+    torch.cuda.empty_cache()
+    return dict(value=value, ms_per_step=ms_per_step, bytes_per_call=P * n * B, B=B, roofline=roof,
+                wall_ms_per_step=wall * 1e3 / steps, event_ms_per_step=ev_ms / steps)
+
+
+def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=32):
+    """The oracle (single-threaded C) on a bounded sample of the workload:
+    a message 1/frac_den the size (every segment shortened alike), drawn from
+    the same Laplace(0,1) recipe, timed over one whole call."""
+    import numpy as np
+    import oracle
+    from error_feedback_quant_amd import inputs
+    S = n // P
+    L = S // frac_den // G * G            # sampled elements per segment
+    # each rank's sample: P segments of L elements from the same Laplace(0,1)
+    # generator (the CPU generator's stream; the distribution is the workload's)
+    sample = [inputs.as_numpy_u16(inputs.laplace(r, P * L, device="cpu", chunk=1 << 24)) for r in range(P)]
+    m = sample[0].size
+    comps = [np.zeros(m, np.float32) for _ in range(P)] if ef else None
+    t0 = time.perf_counter()
+    oracle.allreduce(sample, bits=bits, ef=ef, comps=comps,
+                     out_dtype=oracle.OUT_BF16 if out_bf16 else oracle.OUT_F32)
+    dt = time.perf_counter() - t0
+    B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4)
+    return {"value": round(P * m * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one call on {m} of {n} elements per rank (1/{frac_den} of every segment, "
+                      f"same distribution), P={P}, {dt:.2f} s single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--P", type=int, default=4)
+    ap.add_argument("--bits", type=int, default=4, choices=[4, 8])
+    ap.add_argument("--tiles", type=int, default=8)
+    ap.add_argument("--streams", type=int, default=4)
+    ap.add_argument("--out", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--no-ef", action="store_true")
+    ap.add_argument("--no-p8", action="store_true", help="skip the P=8 leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (the P ranks are simulated on it); "
+              f"--gpus {a.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: one process, one GPU; not for torch.distributed launch", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from error_feedback_quant_amd import echo, inputs
+    assert torch.cuda.is_available(), "no GPU visible"
+
+    out_bf16 = a.out == "bf16"
+    ef = not a.no_ef
+    main_res = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, a.steps, a.warmup,
+                        out_bf16, ef)
+    p8 = None
+    if not a.no_p8 and a.P != 8:
+        r8 = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 2),
+                      a.warmup, out_bf16, ef)
+        p8 = {"value": round(r8["value"], 1), "ms_per_step": round(r8["ms_per_step"], 4),
+              "frac_of_peak": round(r8["value"] / HBM_PEAK_GBS, 4), "roofline": r8["roofline"]}
+    if a.calib_copy:
+        src = torch.empty(N_1GIB, dtype=torch.int16, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(a.P, N_1GIB, a.bits, out_bf16, ef)
+
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"1 GiB message: 2^29 bf16 elements per rank, Laplace(0,1), P={a.P} simulated ranks",
+            "P": a.P, "bits": a.bits, "group": G, "tiles": a.tiles, "streams": a.streams,
+            "ef": "classic error feedback (alpha=1), -e written in place" if ef else "off",
+            "out": a.out, "bytes_per_elem_per_rank": round(main_res["B"], 5),
+            "bytes_per_call": int(main_res["bytes_per_call"]),
+            "frac_of_peak": round(main_res["value"] / HBM_PEAK_GBS, 4),
+        },
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "p8": p8,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

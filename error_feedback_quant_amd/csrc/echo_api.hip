@@ -1,0 +1,452 @@
+// echo_api.hip — host side of libecho: argument checks, kernel launches and
+// the tile-staged multi-stream schedule of one simulated all-reduce call.
+//
+// The calls follow the problem statement of "Echo: Error-Compensated 4-Bit
+// Tensor-Parallel Communication for LLM Training and Inference" (arXiv
+// 2610.14277): Fig. 2(a) (push, owner reduce, quantized all-gather, decode),
+// Fig. 2(b) (tiles staggered across push, reduce, gather and tail, with
+// events ordering the work inside one GPU), and the PhantomByte article's
+// "The cancellation rule" (compensator fused into the entry pass, update run
+// beside the next matmul).  Semantics, layouts and error behaviour are
+// specified in include/echo.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "echo.h"
+#include "echo_kernels.hpp"
+
+namespace {
+
+thread_local int t_last_hip_error = 0;
+
+constexpr int64_t kMaxN = int64_t(1) << 34;
+constexpr int kU = 2;  // groups per row per block (passes of 16 groups)
+
+int hip_fail(hipError_t e)
+{
+    t_last_hip_error = (int)e;
+    return ECHO_EHIP;
+}
+
+int check_launch()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ECHO_OK : hip_fail(e);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t code_bytes(int64_t n, int bits) { return bits == 4 ? n / 2 : n; }
+
+int check_common(int64_t n, int P, int64_t tile_begin, int64_t tile_len, int bits, int group)
+{
+    if (P < 1 || P > ECHO_MAX_P) return ECHO_EINVAL;
+    if (bits != 4 && bits != 8) return ECHO_EUNSUP;
+    if (group != echo::kGroup) return ECHO_EUNSUP;
+    if (n < 0 || n > kMaxN || n % ((int64_t)P * group) != 0) return ECHO_ESHAPE;
+    const int64_t S = n / P;
+    if (tile_begin < 0 || tile_len < 0 || tile_begin % group || tile_len % group ||
+        tile_begin + tile_len > S)
+        return ECHO_ESHAPE;
+    return ECHO_OK;
+}
+
+// alpha, beta ranges; alpha < 1 needs a slow memory to keep the rest of the debt
+int check_alpha_beta(float alpha, float beta)
+{
+    if (!(alpha > 0.0f && alpha <= 1.0f)) return ECHO_EINVAL;
+    if (!(beta >= 0.0f && beta <= 1.0f)) return ECHO_EINVAL;
+    if (alpha < 1.0f && beta == 0.0f) return ECHO_EINVAL;
+    return ECHO_OK;
+}
+
+// the slow memory is given exactly when it is released (beta > 0)
+int check_slow(float beta, bool has_slow) { return has_slow == (beta > 0.0f) ? ECHO_OK : ECHO_EINVAL; }
+
+unsigned blocks_for(uint32_t tile_groups) { return (tile_groups + echo::kRowsPerBlock * kU - 1) / (echo::kRowsPerBlock * kU); }
+
+// ---------------------------------------------------------------- launchers --
+// Each assumes validated arguments and tile_len > 0.
+
+int launch_push(const uint16_t* x, const float* comp, int64_t n, int P, int rank, int64_t tb,
+                int64_t tl, int bits, uint8_t* codes, echo_qparam* params, float* err, int flags,
+                hipStream_t st)
+{
+    if (P == 1) return ECHO_OK;   // a single rank owns everything: nothing to push
+    echo::PushArgs a;
+    a.x = x; a.comp = comp; a.codes = codes; a.params = (uint32_t*)params; a.err = err;
+    a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
+    a.rank = rank; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    dim3 grid(blocks_for(a.tile_groups), (unsigned)(P - 1));
+    if (bits == 4) hipLaunchKernelGGL((echo::push_kernel<4, kU>), grid, dim3(echo::kBlock), 0, st, a);
+    else hipLaunchKernelGGL((echo::push_kernel<8, kU>), grid, dim3(echo::kBlock), 0, st, a);
+    return check_launch();
+}
+
+template <int BITS>
+void launch_reduce_p(const echo::ReduceArgs& a, int P, dim3 grid, hipStream_t st)
+{
+    switch (P) {
+    case 1: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 1, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 2, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 3, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 4, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 5, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 6, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 7: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 7, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    default: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 8, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    }
+}
+
+int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc,
+                  const echo_qparam* const* pp, int P, int owner, int64_t n, int64_t tb, int64_t tl,
+                  int bits, uint8_t* sc, echo_qparam* sp, float* err, int flags, hipStream_t st)
+{
+    echo::ReduceArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x; a.comp = comp;
+    for (int j = 0; j < P; ++j) {
+        a.pc[j] = j == owner ? nullptr : pc[j];
+        a.pp[j] = j == owner ? nullptr : (const uint32_t*)pp[j];
+    }
+    a.sc = sc; a.sp = (uint32_t*)sp; a.err = err;
+    a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
+    a.owner = owner; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    dim3 grid(blocks_for(a.tile_groups), 1);
+    if (bits == 4) launch_reduce_p<4>(a, P, grid, st);
+    else launch_reduce_p<8>(a, P, grid, st);
+    return check_launch();
+}
+
+int launch_gather(const uint8_t* sc, const echo_qparam* sp, int64_t n, int64_t tb, int64_t tl, int P,
+                  int bits, void* out, int out_dtype, hipStream_t st)
+{
+    echo::GatherArgs a;
+    a.sc = sc; a.sp = (const uint32_t*)sp; a.out = out;
+    a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
+    dim3 grid(blocks_for(a.tile_groups), (unsigned)P);
+    const bool bf = out_dtype == ECHO_OUT_BF16;
+    if (bits == 4) {
+        if (bf) hipLaunchKernelGGL((echo::gather_kernel<4, true, kU>), grid, dim3(echo::kBlock), 0, st, a);
+        else hipLaunchKernelGGL((echo::gather_kernel<4, false, kU>), grid, dim3(echo::kBlock), 0, st, a);
+    } else {
+        if (bf) hipLaunchKernelGGL((echo::gather_kernel<8, true, kU>), grid, dim3(echo::kBlock), 0, st, a);
+        else hipLaunchKernelGGL((echo::gather_kernel<8, false, kU>), grid, dim3(echo::kBlock), 0, st, a);
+    }
+    return check_launch();
+}
+
+int launch_compensate(const float* err, float* comp, float* slow, int64_t n, float alpha, float beta,
+                      hipStream_t st)
+{
+    if (n == 0) return ECHO_OK;
+    echo::CompArgs a;
+    a.err = err; a.comp = comp; a.slow = slow; a.n = n;
+    a.alpha = alpha; a.beta = beta;
+    a.one_minus_alpha = 1.0f - alpha;
+    a.one_minus_beta = 1.0f - beta;
+    int64_t chunks = (n + 3) / 4;
+    int64_t blocks = (chunks + echo::kBlock - 1) / echo::kBlock;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    if (slow) hipLaunchKernelGGL((echo::compensate_kernel<true>), dim3((unsigned)blocks), dim3(echo::kBlock), 0, st, a);
+    else hipLaunchKernelGGL((echo::compensate_kernel<false>), dim3((unsigned)blocks), dim3(echo::kBlock), 0, st, a);
+    return check_launch();
+}
+
+// ------------------------------------------------------------- event pool --
+// Cross-stream ordering inside one call uses events from a per-thread,
+// per-device pool (created once, reused by later calls of the same thread).
+
+// The pool is not destroyed at thread exit: the HIP runtime may already be
+// torn down by then, and the process releases the events anyway.
+struct EventPool {
+    int device = -1;
+    std::vector<hipEvent_t> ev;
+};
+thread_local EventPool t_pool;
+
+int get_events(size_t count, hipEvent_t** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (t_pool.device != dev) {
+        for (hipEvent_t ev : t_pool.ev) (void)hipEventDestroy(ev);
+        t_pool.ev.clear();
+        t_pool.device = dev;
+    }
+    while (t_pool.ev.size() < count) {
+        hipEvent_t ev;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e);
+        t_pool.ev.push_back(ev);
+    }
+    *out = t_pool.ev.data();
+    return ECHO_OK;
+}
+
+struct SimLayout {
+    int64_t cb, pbytes, cb_al, pb_al;
+    size_t total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+SimLayout sim_layout(int P, int64_t n, int bits, int group)
+{
+    SimLayout L;
+    L.cb = code_bytes(n, bits);
+    L.pbytes = (n / group) * (int64_t)sizeof(echo_qparam);
+    L.cb_al = (int64_t)align256((size_t)L.cb);
+    L.pb_al = (int64_t)align256((size_t)L.pbytes);
+    L.total = (size_t)(P + 1) * (size_t)(L.cb_al + L.pb_al);
+    return L;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+
+extern "C" {
+
+const char* echo_status_str(int status)
+{
+    switch (status) {
+    case ECHO_OK: return "ok";
+    case ECHO_EINVAL: return "invalid argument";
+    case ECHO_EALIGN: return "pointer not 16-byte aligned";
+    case ECHO_EUNSUP: return "unsupported bits, group or output dtype";
+    case ECHO_ESHAPE: return "invalid message or tile shape";
+    case ECHO_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int echo_last_hip_error(void) { return t_last_hip_error; }
+
+int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P, int rank,
+                     int64_t tile_begin, int64_t tile_len, int bits, int group, uint8_t* codes,
+                     echo_qparam* params, float* err, int flags, void* stream)
+{
+    int rc = check_common(n, P, tile_begin, tile_len, bits, group);
+    if (rc) return rc;
+    if (rank < 0 || rank >= P) return ECHO_EINVAL;
+    if (flags & ~ECHO_ERR_NEGATED) return ECHO_EINVAL;
+    if (n == 0 || tile_len == 0 || P == 1) return ECHO_OK;
+    if (!x_bf16 || !codes || !params) return ECHO_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(params) ||
+        (comp && !aligned16(comp)) || (err && !aligned16(err)))
+        return ECHO_EALIGN;
+    return launch_push(x_bf16, comp, n, P, rank, tile_begin, tile_len, bits, codes, params, err, flags,
+                       (hipStream_t)stream);
+}
+
+int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
+                        const uint8_t* const* peer_codes, const echo_qparam* const* peer_params, int P,
+                        int owner, int64_t n, int64_t tile_begin, int64_t tile_len, int bits, int group,
+                        uint8_t* sum_codes, echo_qparam* sum_params, float* own_err, int flags,
+                        void* stream)
+{
+    int rc = check_common(n, P, tile_begin, tile_len, bits, group);
+    if (rc) return rc;
+    if (owner < 0 || owner >= P) return ECHO_EINVAL;
+    if (flags & ~ECHO_ERR_NEGATED) return ECHO_EINVAL;
+    if (n == 0 || tile_len == 0) return ECHO_OK;
+    if (!own_x_bf16 || !sum_codes || !sum_params) return ECHO_EINVAL;
+    if (P > 1 && (!peer_codes || !peer_params)) return ECHO_EINVAL;
+    for (int j = 0; j < P; ++j) {
+        if (j == owner) continue;
+        if (!peer_codes[j] || !peer_params[j]) return ECHO_EINVAL;
+        if (!aligned16(peer_codes[j]) || !aligned16(peer_params[j])) return ECHO_EALIGN;
+    }
+    if (!aligned16(own_x_bf16) || !aligned16(sum_codes) || !aligned16(sum_params) ||
+        (own_comp && !aligned16(own_comp)) || (own_err && !aligned16(own_err)))
+        return ECHO_EALIGN;
+    return launch_reduce(own_x_bf16, own_comp, peer_codes, peer_params, P, owner, n, tile_begin, tile_len,
+                         bits, sum_codes, sum_params, own_err, flags, (hipStream_t)stream);
+}
+
+int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params, int64_t n,
+                        int64_t tile_begin, int64_t tile_len, int P, int bits, int group, void* out,
+                        int out_dtype, void* stream)
+{
+    int rc = check_common(n, P, tile_begin, tile_len, bits, group);
+    if (rc) return rc;
+    if (out_dtype != ECHO_OUT_F32 && out_dtype != ECHO_OUT_BF16) return ECHO_EUNSUP;
+    if (n == 0 || tile_len == 0) return ECHO_OK;
+    if (!sum_codes || !sum_params || !out) return ECHO_EINVAL;
+    if (!aligned16(sum_codes) || !aligned16(sum_params) || !aligned16(out)) return ECHO_EALIGN;
+    return launch_gather(sum_codes, sum_params, n, tile_begin, tile_len, P, bits, out, out_dtype,
+                         (hipStream_t)stream);
+}
+
+int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n, float alpha, float beta,
+                    void* stream)
+{
+    if (n < 0 || n > kMaxN) return ECHO_ESHAPE;
+    int rc = check_alpha_beta(alpha, beta);
+    if (rc) return rc;
+    if (n == 0) return ECHO_OK;
+    if ((rc = check_slow(beta, slow != nullptr))) return rc;
+    if (!err || !comp_next) return ECHO_EINVAL;
+    if (!aligned16(err) || !aligned16(comp_next) || (slow && !aligned16(slow))) return ECHO_EALIGN;
+    return launch_compensate(err, comp_next, slow, n, alpha, beta, (hipStream_t)stream);
+}
+
+size_t echo_allreduce_sim_workspace_bytes(int P, int64_t n, int bits, int group)
+{
+    if (check_common(n, P, 0, 0, bits, group)) return 0;
+    return sim_layout(P, n, bits, group).total;
+}
+
+int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstreams)
+{
+    if (!a) return ECHO_EINVAL;
+    const int P = a->P;
+    int rc = check_common(a->n, P, 0, 0, a->bits, a->group);
+    if (rc) return rc;
+    if (a->out_dtype != ECHO_OUT_F32 && a->out_dtype != ECHO_OUT_BF16) return ECHO_EUNSUP;
+    if (a->tiles < 1) return ECHO_EINVAL;
+    if (a->ef != 0 && a->ef != 1) return ECHO_EINVAL;
+    if (streams && nstreams < 1) return ECHO_EINVAL;
+    const int64_t n = a->n;
+    if (n == 0) return ECHO_OK;
+    const int64_t S = n / P;
+    bool fused = false;
+    if (a->ef) {
+        bool any_err = false, all_err = true;
+        for (int r = 0; r < P; ++r) {
+            any_err = any_err || a->err[r] != nullptr;
+            all_err = all_err && a->err[r] != nullptr;
+        }
+        if (any_err && !all_err) return ECHO_EINVAL;
+        fused = !any_err;
+        if (fused && !(a->alpha == 1.0f && a->beta == 0.0f)) return ECHO_EINVAL;
+        bool slow_all = true, slow_any = false;
+        for (int r = 0; r < P; ++r) {
+            slow_all = slow_all && a->slow[r] != nullptr;
+            slow_any = slow_any || a->slow[r] != nullptr;
+        }
+        if (slow_any && !slow_all) return ECHO_EINVAL;
+        if ((rc = check_alpha_beta(a->alpha, a->beta))) return rc;
+        if ((rc = check_slow(a->beta, slow_all))) return rc;
+    }
+    for (int r = 0; r < P; ++r) {
+        if (!a->x[r] || !a->out[r]) return ECHO_EINVAL;
+        if (a->ef && !a->comp[r]) return ECHO_EINVAL;
+        if (!aligned16(a->x[r]) || !aligned16(a->out[r])) return ECHO_EALIGN;
+        if (a->ef && (!aligned16(a->comp[r]) || (a->err[r] && !aligned16(a->err[r])) ||
+                      (a->slow[r] && !aligned16(a->slow[r]))))
+            return ECHO_EALIGN;
+    }
+    const SimLayout L = sim_layout(P, n, a->bits, a->group);
+    if (!a->workspace || a->workspace_bytes < L.total) return ECHO_EINVAL;
+    if (!aligned16(a->workspace)) return ECHO_EALIGN;
+
+    // workspace: push codes of every rank, push params of every rank, sum codes, sum params
+    uint8_t* ws = (uint8_t*)a->workspace;
+    const uint8_t* pc[ECHO_MAX_P];
+    const echo_qparam* pp[ECHO_MAX_P];
+    for (int r = 0; r < P; ++r) {
+        pc[r] = ws + (size_t)r * L.cb_al;
+        pp[r] = (const echo_qparam*)(ws + (size_t)P * L.cb_al + (size_t)r * L.pb_al);
+    }
+    uint8_t* sc = ws + (size_t)P * (L.cb_al + L.pb_al);
+    echo_qparam* sp = (echo_qparam*)(sc + L.cb_al);
+
+    // tiles: equal lengths (multiples of the group), the last one ragged
+    const int64_t groups_per_seg = S / a->group;
+    int64_t T = a->tiles;
+    if (T > groups_per_seg) T = groups_per_seg;
+    const int64_t tile_groups = (groups_per_seg + T - 1) / T;
+    const int64_t tile_len = tile_groups * a->group;
+    T = (S + tile_len - 1) / tile_len;
+
+    const int nst = streams ? nstreams : 1;
+    hipStream_t st_main = streams ? (hipStream_t)streams[0] : (hipStream_t)0;
+    auto stage_stream = [&](int stage) -> hipStream_t {
+        return streams ? (hipStream_t)streams[stage % nst] : (hipStream_t)0;
+    };
+    const hipStream_t s_push = stage_stream(0), s_red = stage_stream(1), s_tail = stage_stream(2),
+                      s_comp = stage_stream(3);
+    const bool multi = nst > 1;
+
+    // events: start, per tile push-done and reduce-done, per stream done
+    hipEvent_t* ev = nullptr;
+    if (multi) {
+        rc = get_events((size_t)(1 + 2 * T + 4), &ev);
+        if (rc) return rc;
+    }
+    hipEvent_t ev_start = multi ? ev[0] : nullptr;
+    auto ev_push = [&](int64_t t) { return ev[1 + 2 * t]; };
+    auto ev_red = [&](int64_t t) { return ev[2 + 2 * t]; };
+    hipEvent_t* ev_done = multi ? ev + 1 + 2 * T : nullptr;
+
+    hipError_t he;
+    hipStream_t used[4] = {s_push, s_red, s_tail, s_comp};
+    if (multi) {
+        if ((he = hipEventRecord(ev_start, st_main)) != hipSuccess) return hip_fail(he);
+        for (int k = 0; k < 4 && k < nst; ++k)
+            if (used[k] != st_main && (he = hipStreamWaitEvent(used[k], ev_start, 0)) != hipSuccess)
+                return hip_fail(he);
+    }
+
+    const int flags = fused ? ECHO_ERR_NEGATED : 0;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t tb = t * tile_len;
+        const int64_t tl = (tb + tile_len <= S) ? tile_len : S - tb;
+        // push: every rank quantizes its non-owned segments of this tile
+        for (int r = 0; r < P; ++r) {
+            const float* c = a->ef ? a->comp[r] : nullptr;
+            float* e = a->ef ? (fused ? a->comp[r] : a->err[r]) : nullptr;
+            rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, (uint8_t*)pc[r], (echo_qparam*)pp[r], e,
+                             flags, s_push);
+            if (rc) return rc;
+        }
+        if (multi) {
+            if ((he = hipEventRecord(ev_push(t), s_push)) != hipSuccess) return hip_fail(he);
+            if ((he = hipStreamWaitEvent(s_red, ev_push(t), 0)) != hipSuccess) return hip_fail(he);
+        }
+        // reduce: every owner sums its segment of this tile and requantizes once
+        for (int o = 0; o < P; ++o) {
+            const float* c = a->ef ? a->comp[o] : nullptr;
+            float* e = a->ef ? (fused ? a->comp[o] : a->err[o]) : nullptr;
+            rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, sc, sp, e, flags, s_red);
+            if (rc) return rc;
+        }
+        if (multi) {
+            if ((he = hipEventRecord(ev_red(t), s_red)) != hipSuccess) return hip_fail(he);
+            if ((he = hipStreamWaitEvent(s_tail, ev_red(t), 0)) != hipSuccess) return hip_fail(he);
+        }
+        // gather moves no bytes here; tail: every rank decodes this tile of every segment
+        for (int r = 0; r < P; ++r) {
+            rc = launch_gather(sc, sp, n, tb, tl, P, a->bits, a->out[r], a->out_dtype, s_tail);
+            if (rc) return rc;
+        }
+    }
+    // compensator update (two-timescale or unfused) after the last reduce
+    if (a->ef && !fused) {
+        if (multi && s_comp != s_red) {
+            if ((he = hipStreamWaitEvent(s_comp, ev_red(T - 1), 0)) != hipSuccess) return hip_fail(he);
+        }
+        for (int r = 0; r < P; ++r) {
+            rc = launch_compensate(a->err[r], a->comp[r], a->slow[r], n, a->alpha, a->beta, s_comp);
+            if (rc) return rc;
+        }
+    }
+    if (multi) {
+        for (int k = 0; k < 4 && k < nst; ++k) {
+            if (used[k] == st_main) continue;
+            if ((he = hipEventRecord(ev_done[k], used[k])) != hipSuccess) return hip_fail(he);
+            if ((he = hipStreamWaitEvent(st_main, ev_done[k], 0)) != hipSuccess) return hip_fail(he);
+        }
+    }
+    return ECHO_OK;
+}
+
+}  // extern "C"

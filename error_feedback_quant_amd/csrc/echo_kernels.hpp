@@ -1,0 +1,464 @@
+// echo_kernels.hpp — gfx950 (CDNA4) kernels for Echo's error-compensated
+// low-bit all-reduce, one simulated rank or owner per launch.
+//
+// Method: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for LLM
+// Training and Inference" (arXiv 2610.14277), paper card Fig. 2(a), Fig. 4,
+// Table 8 and abstract; PhantomByte article on Echo, "The cancellation rule".
+//
+// Layout and mapping (all kernels):
+//  * A quantization group is 128 consecutive bf16 elements = 16 lanes x 8
+//    elements, i.e. one 16-lane DPP row of a 64-lane wavefront; each lane
+//    moves its 8 elements with one 16-byte load (bf16) or two (fp32).
+//  * Group min/max are reduced inside the row with four DPP steps
+//    (quad_perm xor-1, xor-2, row_ror 4, row_ror 8): no LDS, no barrier.
+//    min/max are exact and order-free, so the tree cannot change results.
+//  * Every lane of a row derives the group's scale and zero point itself
+//    (same inputs, same IEEE operations), so nothing is broadcast; lane 0 of
+//    the row stores the 4-byte parameter word.
+//  * A 256-thread block handles 16 consecutive groups per pass and U passes;
+//    blockIdx.y selects the segment.  All loads of a block's U passes are
+//    issued before any arithmetic to keep enough bytes in flight for HBM.
+//  * Codes are packed in registers: 8 nibbles -> one dword (4-bit) or 8
+//    bytes -> two dwords (8-bit), so a wavefront writes 256 / 512 contiguous
+//    bytes per pass.
+// Arithmetic is IEEE fp32 with no contraction (built with -ffp-contract=off):
+// the division for the scale and 1/s are correctly rounded; rint rounds half
+// to even; binary16 conversion is the hardware v_cvt_f16_f32 (round to
+// nearest even, binary16 subnormals kept).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace echo {
+
+constexpr int kGroup = 128;
+constexpr int kEPL = 8;                        // elements per lane
+constexpr int kRowLanes = kGroup / kEPL;       // 16 lanes = one DPP row
+constexpr int kBlock = 256;                    // 4 wavefronts of 64
+constexpr int kRowsPerBlock = kBlock / kRowLanes;  // 16 groups per pass
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- helpers --
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// min and max over the 16 lanes of a DPP row; every lane ends with the result
+__device__ __forceinline__ void row_minmax(float& lo, float& hi)
+{
+    lo = fminf(lo, dpp_f<0xB1>(lo));  hi = fmaxf(hi, dpp_f<0xB1>(hi));   // quad_perm [1,0,3,2]
+    lo = fminf(lo, dpp_f<0x4E>(lo));  hi = fmaxf(hi, dpp_f<0x4E>(hi));   // quad_perm [2,3,0,1]
+    lo = fminf(lo, dpp_f<0x124>(lo)); hi = fmaxf(hi, dpp_f<0x124>(hi));  // row_ror:4
+    lo = fminf(lo, dpp_f<0x128>(lo)); hi = fmaxf(hi, dpp_f<0x128>(hi));  // row_ror:8
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 w, float* v)
+{
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Group parameters of the zero-aware asymmetric quantizer (Table 8's full
+// method): range widened to contain 0, binary16 scale, integer zero point.
+struct QParams {
+    float s;        // scale as fp32 (exact binary16 value)
+    float inv;      // 1/s, correctly rounded
+    float zf;       // zero point (integer-valued)
+    uint32_t word;  // binary16 scale | binary16 zero << 16
+};
+
+template <int BITS>
+__device__ __forceinline__ QParams make_params(float lo, float hi)
+{
+    constexpr float kQm = (float)((1 << BITS) - 1);
+    const float s32 = (hi - lo) / kQm;
+    uint32_t sb = f32_to_f16_bits(s32);
+    sb = (sb == 0u) ? 1u : sb;             // underflow -> 2^-24
+    sb = (sb == 0x7C00u) ? 0x7BFFu : sb;   // overflow  -> 65504
+    const float s = f16_bits_to_f32(sb);
+    const float inv = 1.0f / s;
+    const float zr = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * inv), 0.0f, kQm);
+    const float zf = (float)(uint32_t)zr;  // through an integer, so a -0 becomes +0
+    const uint32_t zb = f32_to_f16_bits(zf);
+    const bool zero = (hi == lo);          // all-zero group
+    QParams p;
+    p.s = zero ? 0.0f : s;
+    p.inv = zero ? 0.0f : inv;
+    p.zf = zero ? 0.0f : zf;
+    p.word = zero ? 0u : (sb | (zb << 16));
+    return p;
+}
+
+// code of one value as an integer-valued float: clamp(rint(u/s) + z)
+template <int BITS>
+__device__ __forceinline__ float quant1(float u, const QParams& p)
+{
+    constexpr float kQm = (float)((1 << BITS) - 1);
+    return __builtin_amdgcn_fmed3f(__builtin_rintf(u * p.inv) + p.zf, 0.0f, kQm);
+}
+
+// the 8 codes of a lane, packed (4-bit: one dword, 8-bit: two dwords)
+template <int BITS>
+struct Packed;
+template <>
+struct Packed<4> {
+    uint32_t w;
+    __device__ __forceinline__ void pack(const float* q)
+    {
+        w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= (uint32_t)q[i] << (4 * i);
+    }
+    __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
+    {
+        *(uint32_t*)(codes + (e0 >> 1)) = w;
+    }
+    __device__ __forceinline__ void load(const uint8_t* codes, int64_t e0)
+    {
+        w = *(const uint32_t*)(codes + (e0 >> 1));
+    }
+    __device__ __forceinline__ void unpack(float* q) const
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = (float)((w >> (4 * i)) & 0xFu);
+    }
+};
+template <>
+struct Packed<8> {
+    u32x2 w;
+    __device__ __forceinline__ void pack(const float* q)
+    {
+        w.x = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
+        w.y = (uint32_t)q[4] | ((uint32_t)q[5] << 8) | ((uint32_t)q[6] << 16) | ((uint32_t)q[7] << 24);
+    }
+    __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
+    {
+        *(u32x2*)(codes + e0) = w;
+    }
+    __device__ __forceinline__ void load(const uint8_t* codes, int64_t e0)
+    {
+        w = *(const u32x2*)(codes + e0);
+    }
+    __device__ __forceinline__ void unpack(float* q) const
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (float)((w.x >> (8 * i)) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[4 + i] = (float)((w.y >> (8 * i)) & 0xFFu);
+    }
+};
+
+// Quantize the lane's 8 values of one group (the whole row cooperates),
+// store codes and parameters, and optionally the error (q - z) * s - u.
+template <int BITS>
+__device__ __forceinline__ void quantize_store(const float* u, bool active, uint32_t l16, int64_t e0,
+                                               uint8_t* codes, uint32_t* params, float* err,
+                                               bool negate)
+{
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { lo = fminf(lo, u[i]); hi = fmaxf(hi, u[i]); }
+    row_minmax(lo, hi);
+    const QParams p = make_params<BITS>(lo, hi);
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quant1<BITS>(u[i], p);
+    if (!active) return;
+    Packed<BITS> pk;
+    pk.pack(q);
+    pk.store(codes, e0);
+    if (l16 == 0) params[e0 >> 7] = p.word;
+    if (err) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = (q[i] - p.zf) * p.s - u[i];
+            e[i] = negate ? -v : v;
+        }
+        *(f32x4*)(err + e0) = f32x4{e[0], e[1], e[2], e[3]};
+        *(f32x4*)(err + e0 + 4) = f32x4{e[4], e[5], e[6], e[7]};
+    }
+}
+
+// ------------------------------------------------------- push (entry pass) --
+
+struct PushArgs {
+    const uint16_t* x;
+    const float* comp;      // nullable
+    uint8_t* codes;
+    uint32_t* params;
+    float* err;             // nullable, may alias comp
+    int64_t S;              // segment length
+    int64_t tile_begin;     // tile start inside each segment
+    uint32_t tile_groups;   // groups per segment tile (>= 1)
+    int rank;
+    int negate;
+};
+
+// grid: (ceil(tile_groups / (16 U)), P - 1); blockIdx.y = index among the
+// segments this rank does not own.
+template <int BITS, int U>
+__global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
+{
+    const uint32_t l16 = threadIdx.x & 15u;
+    const uint32_t row = threadIdx.x >> 4;
+    const uint32_t si = blockIdx.y;
+    const uint32_t seg = si + (si >= (uint32_t)a.rank ? 1u : 0u);
+    const int64_t seg0 = (int64_t)seg * a.S + a.tile_begin;
+    const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
+
+    u32x4 xv[U];
+    f32x4 c0[U], c1[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_groups - 1u);
+        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        xv[k] = *(const u32x4*)(a.x + e0);
+        if (a.comp) {
+            c0[k] = *(const f32x4*)(a.comp + e0);
+            c1[k] = *(const f32x4*)(a.comp + e0 + 4);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
+        const bool active = graw < a.tile_groups;
+        const uint32_t gi = min(graw, a.tile_groups - 1u);
+        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        float u[8];
+        unpack_bf16x8(xv[k], u);
+        if (a.comp) {
+            u[0] += c0[k].x; u[1] += c0[k].y; u[2] += c0[k].z; u[3] += c0[k].w;
+            u[4] += c1[k].x; u[5] += c1[k].y; u[6] += c1[k].z; u[7] += c1[k].w;
+        }
+        quantize_store<BITS>(u, active, l16, e0, a.codes, a.params, a.err, a.negate != 0);
+    }
+}
+
+// ------------------------------------------------------------ owner reduce --
+
+struct ReduceArgs {
+    const uint16_t* x;              // owner's partial sums
+    const float* comp;              // owner's compensation, nullable
+    const uint8_t* pc[8];           // push codes of each rank ([owner] unused)
+    const uint32_t* pp[8];          // push parameters of each rank
+    uint8_t* sc;                    // sum codes (message-shaped)
+    uint32_t* sp;                   // sum parameters
+    float* err;                     // owner's error, nullable, may alias comp
+    int64_t S;
+    int64_t tile_begin;
+    uint32_t tile_groups;
+    int owner;
+    int negate;
+};
+
+// grid: (ceil(tile_groups / (16 U)), 1)
+template <int BITS, int P, int U>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
+{
+    const uint32_t l16 = threadIdx.x & 15u;
+    const uint32_t row = threadIdx.x >> 4;
+    const int64_t seg0 = (int64_t)a.owner * a.S + a.tile_begin;
+    const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
+
+    u32x4 xv[U];
+    f32x4 c0[U], c1[U];
+    Packed<BITS> pk[U][P];
+    uint32_t pw[U][P];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_groups - 1u);
+        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        xv[k] = *(const u32x4*)(a.x + e0);
+        if (a.comp) {
+            c0[k] = *(const f32x4*)(a.comp + e0);
+            c1[k] = *(const f32x4*)(a.comp + e0 + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            if (j != a.owner) {
+                pk[k][j].load(a.pc[j], e0);
+                pw[k][j] = a.pp[j][e0 >> 7];
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
+        const bool active = graw < a.tile_groups;
+        const uint32_t gi = min(graw, a.tile_groups - 1u);
+        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        float own[8];
+        unpack_bf16x8(xv[k], own);
+        if (a.comp) {
+            own[0] += c0[k].x; own[1] += c0[k].y; own[2] += c0[k].z; own[3] += c0[k].w;
+            own[4] += c1[k].x; own[5] += c1[k].y; own[6] += c1[k].z; own[7] += c1[k].w;
+        }
+        // fp32 sum in rank order; the owner's own term enters unquantized
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            float t[8];
+            if (j == a.owner) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = own[i];
+            } else {
+                const float s = f16_bits_to_f32(pw[k][j] & 0xFFFFu);
+                const float zf = f16_bits_to_f32(pw[k][j] >> 16);
+                float q[8];
+                pk[k][j].unpack(q);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = (q[i] - zf) * s;
+            }
+            if (j == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = t[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = acc[i] + t[i];
+            }
+        }
+        quantize_store<BITS>(acc, active, l16, e0, a.sc, a.sp, a.err, a.negate != 0);
+    }
+}
+
+// ------------------------------------------------------ gather / tail decode --
+
+struct GatherArgs {
+    const uint8_t* sc;
+    const uint32_t* sp;
+    void* out;
+    int64_t S;
+    int64_t tile_begin;
+    uint32_t tile_groups;
+};
+
+// grid: (ceil(tile_groups / (16 U)), P); blockIdx.y = segment
+template <int BITS, bool OUT_BF16, int U>
+__global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
+{
+    const uint32_t l16 = threadIdx.x & 15u;
+    const uint32_t row = threadIdx.x >> 4;
+    const int64_t seg0 = (int64_t)blockIdx.y * a.S + a.tile_begin;
+    const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
+
+    Packed<BITS> pk[U];
+    uint32_t pw[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_groups - 1u);
+        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        pk[k].load(a.sc, e0);
+        pw[k] = a.sp[e0 >> 7];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
+        if (graw >= a.tile_groups) continue;
+        const int64_t e0 = seg0 + (int64_t)graw * kGroup + (int64_t)(l16 * kEPL);
+        const float s = f16_bits_to_f32(pw[k] & 0xFFFFu);
+        const float zf = f16_bits_to_f32(pw[k] >> 16);
+        float q[8], v[8];
+        pk[k].unpack(q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (q[i] - zf) * s;
+        if (OUT_BF16) {
+            u32x4 w;
+            w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2));
+            w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
+            w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
+            w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
+            *(u32x4*)((uint16_t*)a.out + e0) = w;
+        } else {
+            float* o = (float*)a.out + e0;
+            *(f32x4*)o = f32x4{v[0], v[1], v[2], v[3]};
+            *(f32x4*)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+    }
+}
+
+// ------------------------------------------------------------- compensator --
+
+struct CompArgs {
+    const float* err;
+    float* comp;
+    float* slow;        // nullable (beta == 0)
+    int64_t n;
+    float alpha, beta, one_minus_alpha, one_minus_beta;
+};
+
+__device__ __forceinline__ void comp1(const CompArgs& a, float e, float m, float& c_out, float& m_out)
+{
+    const float fa = a.alpha * e;
+    const float fb = a.beta * m;
+    c_out = -(fa + fb);
+    const float m1 = a.one_minus_beta * m;
+    const float m2 = a.one_minus_alpha * e;
+    m_out = m1 + m2;
+}
+
+// grid-stride over float4 chunks, then a scalar tail
+template <bool SLOW>
+__global__ __launch_bounds__(kBlock) void compensate_kernel(const CompArgs a)
+{
+    const int64_t n4 = a.n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) {
+        const f32x4 e = *(const f32x4*)(a.err + 4 * i);
+        float c[4];
+        if (SLOW) {
+            const f32x4 m = *(const f32x4*)(a.slow + 4 * i);
+            float mo[4];
+            comp1(a, e.x, m.x, c[0], mo[0]);
+            comp1(a, e.y, m.y, c[1], mo[1]);
+            comp1(a, e.z, m.z, c[2], mo[2]);
+            comp1(a, e.w, m.w, c[3], mo[3]);
+            *(f32x4*)(a.slow + 4 * i) = f32x4{mo[0], mo[1], mo[2], mo[3]};
+        } else {
+            c[0] = -(a.alpha * e.x); c[1] = -(a.alpha * e.y);
+            c[2] = -(a.alpha * e.z); c[3] = -(a.alpha * e.w);
+        }
+        *(f32x4*)(a.comp + 4 * i) = f32x4{c[0], c[1], c[2], c[3]};
+    }
+    if (blockIdx.x == 0) {
+        const int64_t i = 4 * n4 + threadIdx.x;
+        if (i < a.n) {
+            const float e = a.err[i];
+            if (SLOW) {
+                float c, mo;
+                comp1(a, e, a.slow[i], c, mo);
+                a.slow[i] = mo;
+                a.comp[i] = c;
+            } else {
+                a.comp[i] = -(a.alpha * e);
+            }
+        }
+    }
+}
+
+}  // namespace echo

@@ -66,27 +66,27 @@ def single(rank: int, n: int = 64 * 1024, seed_step: int = 0) -> torch.Tensor:
     return _bf16_bits(x)
 
 
-def chain_channel_scale(hidden: int = 4096, chain_seed: int = 0) -> torch.Tensor:
-    g = _gen(seed_of("chain", 0, 0, 0) + 7 + chain_seed)
-    return torch.exp(torch.randn(hidden, generator=g, dtype=torch.float32))
+def chain_channel_scale(hidden: int = 4096, chain_seed: int = 0, device="cpu") -> torch.Tensor:
+    g = _gen(seed_of("chain", 0, 0, 0) + 7 + chain_seed, device=device)
+    return torch.exp(torch.randn(hidden, generator=g, dtype=torch.float32, device=device))
 
 
 def chain(rank: int, site: int, tokens: int = 2048, hidden: int = 4096,
-          sigma_h: torch.Tensor | None = None, chain_seed: int = 0) -> torch.Tensor:
+          sigma_h: torch.Tensor | None = None, chain_seed: int = 0, device="cpu") -> torch.Tensor:
     if sigma_h is None:
-        sigma_h = chain_channel_scale(hidden, chain_seed)
-    g = _gen(seed_of("chain", chain_seed, site, rank))
-    x = 0.02 * torch.randn(tokens, hidden, generator=g, dtype=torch.float32) * sigma_h
+        sigma_h = chain_channel_scale(hidden, chain_seed, device=device)
+    g = _gen(seed_of("chain", chain_seed, site, rank), device=device)
+    x = 0.02 * torch.randn(tokens, hidden, generator=g, dtype=torch.float32, device=device) * sigma_h
     return _bf16_bits(x.reshape(-1))
 
 
 def chain8(rank: int, site: int, tokens: int = 4096, hidden: int = 1024,
-           chain_seed: int = 0) -> torch.Tensor:
-    g = _gen(seed_of("chain8", chain_seed, site, rank))
+           chain_seed: int = 0, device="cpu") -> torch.Tensor:
+    g = _gen(seed_of("chain8", chain_seed, site, rank), device=device)
     n = tokens * hidden
-    x = 0.05 * torch.randn(n, generator=g, dtype=torch.float32)
-    mask = torch.rand(n, generator=g) < 0.3
-    small = (torch.rand(n, generator=g, dtype=torch.float32) * 2.0 - 1.0) * 1e-3
+    x = 0.05 * torch.randn(n, generator=g, dtype=torch.float32, device=device)
+    mask = torch.rand(n, generator=g, device=device) < 0.3
+    small = (torch.rand(n, generator=g, dtype=torch.float32, device=device) * 2.0 - 1.0) * 1e-3
     x = torch.where(mask, small, x)
     return _bf16_bits(x)
 
@@ -107,13 +107,15 @@ def training(rank: int, step: int, site: int, backward: bool, n: int,
 
 def laplace(rank: int, n: int, device="cpu", chunk: int = 1 << 26, workload: str = "onegb") -> torch.Tensor:
     """Laplace(0, 1) by inversion of a uniform draw, generated in chunks so
-    that the float32 temporaries stay small next to a 1 GiB output."""
+    that the float32 temporaries stay small next to a 1 GiB output.  |u| is
+    kept below 1/2 (a draw of exactly 0 would give log(0) = -inf), which caps
+    |x| at about 17.3."""
     g = _gen(seed_of(workload, 0, 0, rank), device=device)
     out = torch.empty(n, dtype=torch.int16, device=device)
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
         u = torch.rand(b - a, generator=g, dtype=torch.float32, device=device) - 0.5
-        x = -torch.sign(u) * torch.log1p(-2.0 * u.abs())
+        x = -torch.sign(u) * torch.log1p(-2.0 * u.abs().clamp(max=0.5 - 2.0 ** -26))
         out[a:b] = _bf16_bits(x)
         del u, x
     return out

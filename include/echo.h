@@ -1,0 +1,235 @@
+/*
+ * echo.h — C ABI of libecho: the per-call hot path of Echo's
+ * error-compensated low-bit all-reduce, on one MI355X (gfx950).
+ *
+ * Sources: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for
+ * LLM Training and Inference" (arXiv 2610.14277), paper card: abstract,
+ * Fig. 1, Fig. 2(a)/(b), Table 8, appendix Fig. 4; and the PhantomByte article
+ * "Your All-Reduce Is 4x Overpriced: Echo's 4-Bit Error-Feedback Trick for
+ * Tensor-Parallel Training", section "The cancellation rule".
+ *
+ * The problem: P tensor-parallel ranks each hold a partial sum x_r of n
+ * bfloat16 values; the all-reduce returns sum_r x_r to every rank.  Echo
+ * splits the message into P equal contiguous segments, segment s owned by
+ * rank s.  Each rank adds its compensation, quantizes the P-1 segments it
+ * does not own and pushes the codes to their owners; each owner dequantizes
+ * them, adds its own unquantized segment in fp32 and quantizes the sum once;
+ * every rank decodes that same code.  The errors the sum reveals feed a
+ * compensator whose output is added at the next call.
+ *
+ * Here the P ranks are P sets of buffers on one GPU: "push" and "gather"
+ * move no bytes between devices; each simulated rank still performs its own
+ * reads and writes.
+ *
+ * Conventions for every call:
+ *  - Pointers marked (device) are device memory, (host) are host memory.  The
+ *    caller owns every buffer and keeps it alive until the enqueued work is
+ *    done.  The library never allocates or frees device memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue;
+ *    they do not synchronize.
+ *  - Arguments are checked on the host before anything is enqueued; a call
+ *    that returns an error other than ECHO_EHIP has enqueued nothing.
+ *  - Data pointers must be 16-byte aligned (ECHO_EALIGN otherwise).
+ *  - Messages: n elements per rank, 0 <= n <= 2^36, n a multiple of P*group.
+ *    S = n / P is the segment length.  Tiles are element ranges *inside each
+ *    segment*: [tile_begin, tile_begin + tile_len), both multiples of group,
+ *    tile_begin + tile_len <= S.  (0, S) means whole segments.
+ *  - bits is 4 or 8; group is 128 (ECHO_EUNSUP otherwise).  P is 1..8.
+ *  - Codes: unsigned, 0 .. 2^bits - 1.  bits = 4: element i's code is in byte
+ *    i/2, the low nibble when i is even; bits = 8: byte i.  Code arrays are
+ *    message-shaped: n*bits/8 bytes, segment s at byte offset s*S*bits/8.
+ *  - Per-group parameters: one echo_qparam per group of `group` consecutive
+ *    message elements (n/group entries, message-shaped): IEEE binary16 scale s
+ *    and binary16 zero point z (an integer).  Decoding is v = (q - z) * s,
+ *    exact in fp32.
+ *  - Non-finite inputs give unspecified (but memory-safe) results.
+ *  - Thread safety: calls are reentrant.  Calls that write the same buffers
+ *    must be ordered by the caller.
+ */
+#ifndef ECHO_H
+#define ECHO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum echo_status {
+    ECHO_OK = 0,
+    ECHO_EINVAL = -1, /* null required pointer, bad P/rank/owner/constants */
+    ECHO_EALIGN = -2, /* a data pointer is not 16-byte aligned */
+    ECHO_EUNSUP = -3, /* bits not 4/8, group not 128, unknown output dtype */
+    ECHO_ESHAPE = -4, /* n or tile not a valid multiple / out of range */
+    ECHO_EHIP = -5    /* a HIP launch or runtime call failed; see echo_last_hip_error */
+};
+
+enum echo_out_dtype { ECHO_OUT_F32 = 0, ECHO_OUT_BF16 = 1 };
+
+/* flags for echo_quantize_ef / echo_reduce_segment */
+enum { ECHO_ERR_NEGATED = 1 /* write -e (the next call's compensation) instead of e */ };
+
+#define ECHO_MAX_P 8
+
+typedef struct echo_qparam {
+    uint16_t scale_f16; /* binary16 bits of s */
+    uint16_t zero_f16;  /* binary16 bits of the integer zero point z */
+} echo_qparam;
+
+/*
+ * echo_quantize_ef — entry pass and push quantization for one rank.
+ * Paper card Fig. 2(a) and Fig. 4 (each rank quantizes the segments it does
+ * not own, keeps its own); article "The cancellation rule" (the compensation
+ * is added in the entry pass; parameters are half precision per group);
+ * Table 8 (zero-aware asymmetric quantizer, g = 128).
+ *
+ * For every segment s != rank and every group of the tile inside it:
+ *   u = float(x) + comp            (u = float(x) when comp is NULL)
+ *   lo = min(0, min u), hi = max(0, max u)
+ *   s = binary16((hi - lo) / (2^bits - 1)), round to nearest even; a zero
+ *       result becomes 2^-24 and an infinite one 65504; hi == lo (an all-zero
+ *       group) gives s = +0, z = 0 and all codes 0
+ *   z = clamp(rint(-lo * (1/s)), 0, 2^bits - 1)
+ *   q = clamp(rint(u * (1/s)) + z, 0, 2^bits - 1)
+ *   err = (q - z) * s - u          (or its negation with ECHO_ERR_NEGATED)
+ * All float operations are single IEEE fp32 operations (no contraction);
+ * 1/s and the scale division are correctly rounded; rint rounds half to even.
+ *
+ *   x_bf16 (device, in)   bfloat16 bits [n] of this rank's partial sums
+ *   comp   (device, in)   fp32 [n] compensation, or NULL (no feedback)
+ *   codes  (device, out)  this rank's push codes (message-shaped)
+ *   params (device, out)  this rank's push parameters (message-shaped)
+ *   err    (device, out)  fp32 [n] revealed error, or NULL.  May alias comp:
+ *                         each element is read before it is overwritten.
+ * Elements of segment `rank` and outside the tile are not touched.
+ */
+int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P, int rank,
+                     int64_t tile_begin, int64_t tile_len, int bits, int group,
+                     uint8_t* codes, echo_qparam* params, float* err, int flags, void* stream);
+
+/*
+ * echo_reduce_segment — the owner's high-precision sum and single
+ * requantization.  Paper card Fig. 2(a) (the owner dequantizes the received
+ * codes and adds its own unquantized segment in high precision; the reduced
+ * segment is quantized once for the all-gather), Fig. 4, abstract (the sum
+ * reveals each injected error).
+ *
+ * For every group of segment `owner` inside the tile:
+ *   t_j = float(own_x) + own_comp       when j == owner (no quantization)
+ *   t_j = (q_j - z_j) * s_j              from peer j's push codes otherwise
+ *   acc = t_0 + t_1 + ... + t_{P-1}      in fp32, left to right in rank order
+ *   sum codes / params = Q(acc)          (the quantizer of echo_quantize_ef)
+ *   own_err = (q - z) * s - acc          (or its negation with ECHO_ERR_NEGATED)
+ *
+ *   own_x_bf16, own_comp (device, in)  the owner's x and comp (comp nullable)
+ *   peer_codes, peer_params (host arrays of P device pointers, in)
+ *                                      each rank's push codes/params; entry
+ *                                      [owner] is not read and may be NULL
+ *   sum_codes, sum_params (device, out) message-shaped; only segment `owner`
+ *                                      inside the tile is written
+ *   own_err (device, out, nullable)    fp32 [n]; may alias own_comp
+ */
+int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
+                        const uint8_t* const* peer_codes, const echo_qparam* const* peer_params,
+                        int P, int owner, int64_t n, int64_t tile_begin, int64_t tile_len,
+                        int bits, int group, uint8_t* sum_codes, echo_qparam* sum_params,
+                        float* own_err, int flags, void* stream);
+
+/*
+ * echo_gather_dequant — quantized all-gather and tail decode for one rank.
+ * Paper card Fig. 2(a) (every rank, the owner included, decodes the same
+ * code, so all outputs are identical), Fig. 4.
+ *
+ * For every segment and every element of the tile inside it:
+ *   out[i] = (q_i - z) * s   as fp32, or rounded to bfloat16 (nearest even)
+ *
+ *   sum_codes, sum_params (device, in)  the owners' sum codes (message-shaped)
+ *   out (device, out)  fp32 [n] (ECHO_OUT_F32) or bfloat16 bits [n] (ECHO_OUT_BF16)
+ */
+int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params, int64_t n,
+                        int64_t tile_begin, int64_t tile_len, int P, int bits, int group,
+                        void* out, int out_dtype, void* stream);
+
+/*
+ * echo_compensate — the two-timescale compensator update, elementwise.
+ * Paper card abstract (revealed errors are fed back into later calls, so old
+ * errors cancel); article "The cancellation rule" (a two-timescale
+ * compensator; the update runs beside the next matrix multiplication).  The
+ * pages give no equation; the reading is an error debt with a fast fraction
+ * alpha returned at the next call and a slow memory M released at rate beta:
+ *   comp_next = -(alpha*e + beta*M)
+ *   M         = (1-beta)*M + (1-alpha)*e
+ * (products rounded, then the sum, then the negation).  With slow == NULL
+ * (beta must be 0): comp_next = -(alpha*e); alpha = 1 is classic error feedback.
+ *
+ *   err (device, in)        fp32 [n] revealed errors of the last call
+ *   comp_next (device, out) fp32 [n]; may alias err
+ *   slow (device, in/out)   fp32 [n] slow memory M, or NULL
+ * Constraints: 0 < alpha <= 1, 0 <= beta <= 1, beta > 0 iff slow != NULL,
+ * alpha < 1 requires beta > 0 (ECHO_EINVAL otherwise).
+ */
+int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
+                    float alpha, float beta, void* stream);
+
+/*
+ * echo_allreduce_sim — one whole call for P simulated ranks: push, owner
+ * reduce, gather, tail decode and (if on) the compensator update, with each
+ * segment split into `tiles` tiles staggered across streams.  Paper card
+ * Fig. 2(b) (tiles staggered across push, reduce, gather and tail; events
+ * order the work inside a GPU).
+ *
+ * Stage k of every tile runs on streams[k % nstreams] (push 0, reduce 1,
+ * tail 2, compensator 3); events order tile t's reduce after its pushes and
+ * its tail after its reduce.  The gather moves no bytes here: the tail reads
+ * the owners' sum codes directly.  All streams start after the work already
+ * enqueued on streams[0], and streams[0] waits for all of them before the
+ * call returns, so the caller may treat the call as enqueued on streams[0].
+ * streams may be NULL (null stream only).  Results do not depend on tiles or
+ * streams (bit for bit).
+ *
+ * Feedback (ef = 1): every rank's comp is added at the entry pass.  If
+ * alpha == 1, beta == 0 and err[r] == NULL for every rank, the kernels write
+ * -e straight into comp (classic error feedback, bit-identical to running
+ * echo_compensate); otherwise err[r] receives e and echo_compensate turns it
+ * into comp[r] (and slow[r]) after the call's last reduce.
+ *
+ * The workspace (device, caller-allocated, >= echo_allreduce_sim_workspace_bytes)
+ * holds every rank's push codes/params and the sum codes/params.
+ */
+typedef struct echo_sim_args {
+    int P;          /* ranks, 1..8 */
+    int bits;       /* 4 or 8 */
+    int group;      /* 128 */
+    int tiles;      /* tiles per segment, >= 1 (capped at S/group) */
+    int out_dtype;  /* ECHO_OUT_F32 or ECHO_OUT_BF16 */
+    int ef;         /* 0: no compensation; 1: compensation on */
+    float alpha;    /* fast fraction, 0 < alpha <= 1 */
+    float beta;     /* slow release rate, 0 <= beta <= 1 */
+    int64_t n;      /* elements per rank */
+    const uint16_t* x[ECHO_MAX_P]; /* (device) bf16 bits [n] per rank */
+    float* comp[ECHO_MAX_P];       /* (device) fp32 [n] per rank (ef = 1) */
+    float* slow[ECHO_MAX_P];       /* (device) fp32 [n] per rank (beta > 0) */
+    float* err[ECHO_MAX_P];        /* (device) fp32 [n] per rank, or NULL (fused classic) */
+    void* out[ECHO_MAX_P];         /* (device) [n] fp32 or bf16 bits per rank */
+    void* workspace;               /* (device) */
+    size_t workspace_bytes;
+} echo_sim_args;
+
+/* Bytes of workspace echo_allreduce_sim needs; 0 for invalid arguments. */
+size_t echo_allreduce_sim_workspace_bytes(int P, int64_t n, int bits, int group);
+
+/* streams: host array of nstreams hipStream_t handles, or NULL. */
+int echo_allreduce_sim(const echo_sim_args* args, void* const* streams, int nstreams);
+
+/* Static description of a status code. */
+const char* echo_status_str(int status);
+
+/* The hipError_t behind the calling thread's last ECHO_EHIP (0 if none). */
+int echo_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECHO_H */

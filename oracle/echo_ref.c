@@ -411,10 +411,10 @@ int echo_ref_compensate(const float* err, float* comp_next, float* slow, int64_t
 {
     if (n < 0) return REF_ESHAPE;
     if (!(alpha > 0.0f && alpha <= 1.0f) || !(beta >= 0.0f && beta <= 1.0f)) return REF_EINVAL;
-    if (!slow && beta != 0.0f) return REF_EINVAL;
-    if (slow && beta == 0.0f && alpha < 1.0f) return REF_EINVAL;
-    if (alpha < 1.0f && beta == 0.0f) return REF_EINVAL;
-    if ((!err || !comp_next) && n > 0) return REF_EINVAL;
+    if (alpha < 1.0f && beta == 0.0f) return REF_EINVAL;   /* the rest of the debt needs a slow memory */
+    if (n == 0) return REF_OK;
+    if ((slow != NULL) != (beta > 0.0f)) return REF_EINVAL; /* slow memory exactly when released */
+    if (!err || !comp_next) return REF_EINVAL;
     float oma = 1.0f - alpha, omb = 1.0f - beta;
     for (int64_t i = 0; i < n; ++i) {
         float e = err[i];

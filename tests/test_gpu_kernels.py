@@ -1,0 +1,242 @@
+"""GPU parity of each libecho entry point against the CPU oracle.
+
+Each test runs the same seeded inputs through the C ABI on the GPU and
+through the oracle on the host, over the single-call workload's shape (P = 4,
+64 x 1024 per rank) and ragged tiles that leave partial blocks, and compares:
+codes and parameters byte for byte, fp32 errors/outputs within 1e-6 relative
+(the bar for floating point), bf16 outputs bit for bit.  Buffers start filled
+with a sentinel on both sides, so writes outside the tile are caught too.
+Push codes fed to the reduce test come from the oracle, so each kernel is
+checked on its own.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import (DEV, assert_bits_equal, assert_f32_parity, dev_f32, dev_u8, dev_u16, host_f32,
+                      host_u8, host_u16, params_dev, rand_bf16, say)
+from error_feedback_quant_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+P, N = 4, 64 * 1024
+S = N // P
+G = 128
+TILES = [(0, S), (3 * G, S - 5 * G), (S - G, G), (7 * G, 33 * G)]
+
+
+@pytest.fixture(scope="module")
+def echo():
+    from error_feedback_quant_amd import echo as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def single_inputs():
+    return [inputs.as_numpy_u16(inputs.single(r)) for r in range(P)]
+
+
+def sentinel_f32(n):
+    return np.full(n, np.float32(-7.5e-3), dtype=np.float32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("mode", ["plain", "comp_err", "comp_negated_inplace", "err_only", "comp_only"])
+def test_quantize_ef(echo, bits, mode):
+    xs = single_inputs()
+    rng = np.random.default_rng(11 + bits)
+    cb = oracle.code_bytes(N, bits)
+    for rank in range(P):
+        for tb, tl in TILES:
+            say("quantize_ef", bits, mode, rank, tb, tl)
+            comp = (rng.standard_normal(N) * 0.05).astype(np.float32) if "comp" in mode else None
+            want_codes = np.full(cb, 0xAB, np.uint8)
+            want_params = np.full(2 * N // G, 0xCDCD, np.uint16)
+            flags = 0
+            if mode == "comp_negated_inplace":
+                want_err = comp.copy()
+                flags = oracle.ERR_NEGATED
+            elif mode in ("comp_err", "err_only"):
+                want_err = sentinel_f32(N)
+            else:
+                want_err = None
+            oracle.quantize_ef(xs[rank], comp.copy() if comp is not None else None, N, P, rank, tb, tl, bits,
+                               G, want_codes, want_params, want_err, flags)
+            if mode == "comp_negated_inplace":
+                # the oracle's err aliases its own comp copy on the GPU side too
+                pass
+            x_d = dev_u16(xs[rank])
+            comp_d = dev_f32(comp) if comp is not None else None
+            codes_d = dev_u8(np.full(cb, 0xAB, np.uint8))
+            params_d = params_dev(N // G)
+            if mode == "comp_negated_inplace":
+                err_d = comp_d
+            elif want_err is not None:
+                err_d = dev_f32(sentinel_f32(N))
+            else:
+                err_d = None
+            echo.echo_quantize_ef(x_d, comp_d, N, P, rank, tb, tl, bits, G, codes_d, params_d, err_d, flags)
+            torch.cuda.synchronize()
+            assert_bits_equal(host_u8(codes_d), want_codes, "codes")
+            assert_bits_equal(host_u16(params_d), want_params, "params")
+            if want_err is not None:
+                assert_f32_parity(host_f32(err_d), want_err, "err")
+                assert_bits_equal(host_f32(err_d), want_err, "err bits")
+
+
+def oracle_push_all(xs, comps, bits):
+    cb = oracle.code_bytes(N, bits)
+    pc = [np.zeros(cb, np.uint8) for _ in range(P)]
+    pp = [np.zeros(2 * N // G, np.uint16) for _ in range(P)]
+    for r in range(P):
+        oracle.quantize_ef(xs[r], comps[r] if comps else None, N, P, r, 0, S, bits, G, pc[r], pp[r], None)
+    return pc, pp
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("with_comp", [False, True])
+@pytest.mark.parametrize("Pn", [1, 2, 4, 8])
+def test_reduce_segment(echo, bits, with_comp, Pn):
+    n = Pn * 16 * G
+    Sn = n // Pn
+    xs = [rand_bf16(n, 30 + r + 10 * Pn) for r in range(Pn)]
+    rng = np.random.default_rng(3 + Pn)
+    comps = [(rng.standard_normal(n) * 0.05).astype(np.float32) for _ in range(Pn)] if with_comp else None
+    cb = oracle.code_bytes(n, bits)
+    pc = [np.zeros(cb, np.uint8) for _ in range(Pn)]
+    pp = [np.zeros(2 * n // G, np.uint16) for _ in range(Pn)]
+    for r in range(Pn):
+        oracle.quantize_ef(xs[r], comps[r] if comps else None, n, Pn, r, 0, Sn, bits, G, pc[r], pp[r], None)
+    pc_d = [dev_u8(a) for a in pc]
+    pp_d = [dev_u16(a) for a in pp]
+    for owner in range(Pn):
+        for tb, tl in [(0, Sn), (G, Sn - 3 * G), (Sn - G, G)]:
+            for negate in (0, oracle.ERR_NEGATED):
+                say("reduce_segment", bits, with_comp, Pn, owner, tb, tl, negate)
+                sc = np.full(cb, 0x5A, np.uint8)
+                sp = np.full(2 * n // G, 0x1234, np.uint16)
+                err = sentinel_f32(n)
+                oracle.reduce_segment(xs[owner], comps[owner] if comps else None, pc, pp, Pn, owner, n, tb, tl,
+                                      bits, G, sc, sp, err, negate)
+                sc_d = dev_u8(np.full(cb, 0x5A, np.uint8))
+                sp_d = params_dev(n // G, 0x1234)
+                err_d = dev_f32(sentinel_f32(n))
+                echo.echo_reduce_segment(dev_u16(xs[owner]), dev_f32(comps[owner]) if comps else None,
+                                         [None if j == owner else pc_d[j] for j in range(Pn)],
+                                         [None if j == owner else pp_d[j] for j in range(Pn)],
+                                         Pn, owner, n, tb, tl, bits, G, sc_d, sp_d, err_d, negate)
+                torch.cuda.synchronize()
+                assert_bits_equal(host_u8(sc_d), sc, "sum codes")
+                assert_bits_equal(host_u16(sp_d), sp, "sum params")
+                assert_f32_parity(host_f32(err_d), err, "own err")
+                assert_bits_equal(host_f32(err_d), err, "own err bits")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("odt", [oracle.OUT_F32, oracle.OUT_BF16])
+def test_gather_dequant(echo, bits, odt):
+    xs = single_inputs()
+    pc, pp = oracle_push_all(xs, None, bits)
+    cb = oracle.code_bytes(N, bits)
+    sc = np.zeros(cb, np.uint8)
+    sp = np.zeros(2 * N // G, np.uint16)
+    for o in range(P):
+        oracle.reduce_segment(xs[o], None, pc, pp, P, o, N, 0, S, bits, G, sc, sp, None)
+    sc_d, sp_d = dev_u8(sc), dev_u16(sp)
+    for tb, tl in TILES:
+        say("gather_dequant", bits, odt, tb, tl)
+        if odt == oracle.OUT_F32:
+            want = sentinel_f32(N)
+            out_d = dev_f32(sentinel_f32(N))
+        else:
+            want = np.full(N, 0xBEEF, np.uint16)
+            out_d = dev_u16(np.full(N, 0xBEEF, np.uint16))
+        oracle.gather_dequant(sc, sp, N, tb, tl, P, bits, G, want, odt)
+        echo.echo_gather_dequant(sc_d, sp_d, N, tb, tl, P, bits, G, out_d, odt)
+        torch.cuda.synchronize()
+        if odt == oracle.OUT_F32:
+            assert_f32_parity(host_f32(out_d), want, "out")
+            assert_bits_equal(host_f32(out_d), want, "out bits")
+        else:
+            assert_bits_equal(host_u16(out_d), want, "bf16 out")
+
+
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, 0.25), (0.75, 0.1), (0.3, 1.0)])
+@pytest.mark.parametrize("n", [0, 3, 4096, 4096 + 3, 1 << 20])
+def test_compensate(echo, alpha, beta, n):
+    say("compensate", alpha, beta, n)
+    rng = np.random.default_rng(n + int(alpha * 100))
+    e = (rng.standard_normal(n) * 0.01).astype(np.float32)
+    M = (rng.standard_normal(n) * 0.02).astype(np.float32) if beta > 0 else None
+    c = np.full(n, 9.0, np.float32)
+    Mw = M.copy() if M is not None else None
+    oracle.compensate(e, c, Mw, n, alpha, beta)
+    e_d = dev_f32(e)
+    c_d = dev_f32(np.full(n, 9.0, np.float32))
+    M_d = dev_f32(M) if M is not None else None
+    echo.echo_compensate(e_d, c_d, M_d, n, alpha, beta)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_f32(c_d), c, "comp")
+    if M is not None:
+        assert_bits_equal(host_f32(M_d), Mw, "slow")
+    # in place: comp_next aliasing err
+    if n:
+        e2 = dev_f32(e)
+        M2 = dev_f32(M) if M is not None else None
+        echo.echo_compensate(e2, e2, M2, n, alpha, beta)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_f32(e2), c, "comp in place")
+
+
+def edge_groups(bits):
+    """fp32 groups (fed as comp with x = 0, so u = comp exactly) that hit the
+    quantizer's special cases: an all-zero group, one-sided groups (z = 0 and
+    z = Qm), binary16-subnormal and underflowing scales, an overflowing scale
+    (clamped to 65504), exact ties in rint for codes and for the zero point,
+    a scale that is an exact binary16 midpoint, and negative zeros."""
+    Qm = (1 << bits) - 1
+    rng = np.random.default_rng(5)
+    gs = []
+    gs.append(np.zeros(G))
+    z = np.zeros(G); z[::3] = -0.0; gs.append(z)
+    gs.append(np.abs(rng.standard_normal(G)))
+    gs.append(-np.abs(rng.standard_normal(G)))
+    gs.append(rng.standard_normal(G) * 1e-6)                 # subnormal binary16 scale
+    gs.append(rng.standard_normal(G) * 1e-9)                 # scale underflows -> 2^-24
+    gs.append(rng.standard_normal(G) * 1e7)                  # scale overflows -> 65504
+    s = 2.0 ** -4                                            # exact scale, inv = 16
+    lo, hi = -8.0 * s, (Qm - 8.0) * s                        # z = 8 exactly
+    t = np.concatenate([[lo, hi], (np.arange(-8, Qm - 8) + 0.5) * s])  # every code tie
+    gs.append(np.resize(t, G))
+    lo = -8.5 * s; hi = lo + Qm * s                          # zero point tie at 8.5
+    gs.append(np.resize(np.array([lo, hi, 0.0, 0.5 * s, -0.5 * s]), G))
+    mid = 1.0 + 2.0 ** -11                                   # halfway between binary16 1 and 1+2^-10
+    gs.append(np.resize(np.array([0.0, Qm * mid, 3.0, 7.25]), G))
+    gs.append(np.resize(np.array([0.0, Qm * (1.0 + 3 * 2.0 ** -11)]), G))  # the other tie direction
+    gs.append(np.full(G, 3.0))                               # constant nonzero group
+    return [g.astype(np.float32) for g in gs]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_edge_groups(echo, bits):
+    groups = edge_groups(bits)
+    assert len(groups) % P == 0
+    n = G * len(groups)              # the groups spread over the P segments
+    Sn = n // P
+    comp = np.concatenate(groups).astype(np.float32)
+    x = np.zeros(n, np.uint16)
+    for rank in range(P):
+        say("edge groups", bits, rank)
+        cb = oracle.code_bytes(n, bits)
+        wc = np.zeros(cb, np.uint8); wp = np.zeros(2 * n // G, np.uint16); we = np.zeros(n, np.float32)
+        oracle.quantize_ef(x, comp, n, P, rank, 0, Sn, bits, G, wc, wp, we)
+        cd = dev_u8(np.zeros(cb, np.uint8)); pd = params_dev(n // G, 0); ed = dev_f32(np.zeros(n, np.float32))
+        echo.echo_quantize_ef(dev_u16(x), dev_f32(comp), n, P, rank, 0, Sn, bits, G, cd, pd, ed, 0)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u8(cd), wc, "edge codes")
+        assert_bits_equal(host_u16(pd), wp, "edge params")
+        assert_bits_equal(host_f32(ed), we, "edge err")
+    # the scale-tie groups really produced binary16 midpoints and clamps
+    sc = wp[0::2]
+    assert 0x7BFF in set(sc.tolist()) and 0x0001 in set(sc.tolist())

@@ -1,0 +1,187 @@
+"""The workloads at full size on the GPU.
+
+* 1 GiB message (2^29 bf16 per rank, Laplace(0,1)), P = 4 and P = 8, in the
+  launch configuration the benchmark times (bf16 output, classic feedback
+  written in place, tiles staggered over four streams), two consecutive
+  calls.  Sampled parity: the oracle recomputes a set of groups from every
+  segment (an exact sub-problem: quantization, sums and feedback act per
+  group and per element) and must match bit for bit; properties over the
+  whole message: bitwise identical outputs on every rank, and the injected
+  error equals the revealed errors (fed back as -comp) up to fp32 rounding.
+* Depth chains (Echo paper card Fig. 1: N injection sites add their
+  all-reduce output to the hidden state): 4-bit, P = 4, 2048 x 4096, 64 sites,
+  and 8-bit, P = 4, 4096 x 1024, 56 sites.  Each site is checked against the
+  oracle on a row slice that keeps segment ownership (the first rows of every
+  segment); over the whole message the accumulated error must equal the
+  outstanding error debt (-sum of comp), stay bounded with feedback, and grow
+  without it (abstract: bounded independently of depth).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import DEV, assert_bits_equal, host_f32, host_u16, say
+from error_feedback_quant_amd import inputs
+
+pytestmark = pytest.mark.gpu
+G = 128
+U24 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def echo():
+    from error_feedback_quant_amd import echo as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def sample_index(P, S, n_groups, seed):
+    """Element indices (device, int64) of `n_groups` group offsets taken from
+    every segment (same offsets in each segment, so ownership is kept), laid
+    out as a mini message of P * n_groups * 128 elements."""
+    rng = np.random.default_rng(seed)
+    gps = S // G
+    offs = set([0, gps - 1, gps // 2, gps // 3])
+    offs |= set(rng.choice(gps, size=n_groups - len(offs), replace=False).tolist())
+    offs = np.array(sorted(offs)[:n_groups], dtype=np.int64)
+    seg = np.arange(P, dtype=np.int64)[:, None, None] * S
+    idx = seg + offs[None, :, None] * G + np.arange(G, dtype=np.int64)[None, None, :]
+    return torch.from_numpy(idx.reshape(-1)).to(DEV)
+
+
+def bf16_dev_to_f64(t):
+    return t.view(torch.bfloat16).to(torch.float64)
+
+
+@pytest.mark.parametrize("P", [4, 8])
+def test_onegb_sampled_parity_and_identities(echo, P):
+    n = 1 << 29
+    S = n // P
+    tiles, nstreams = 8, 4
+    torch.cuda.empty_cache()
+    say("onegb", P, "generate")
+    xs = [inputs.laplace(r, n, device=DEV) for r in range(P)]
+    comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, 4), dtype=torch.uint8, device=DEV)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+    idx = sample_index(P, S, 48, seed=P)
+    mini_n = idx.numel()
+    o_comps = [np.zeros(mini_n, np.float32) for _ in range(P)]
+    for call in range(2):
+        if call == 1:                       # fresh partials for the second call, same shapes
+            for r in range(P):
+                xs[r] = inputs.laplace(r + 16, n, device=DEV)
+        x_mini = [host_u16(x[idx]) for x in xs]
+        c_before = [c.clone() for c in comps] if call == 1 else None
+        say("onegb", P, "call", call)
+        a = echo.make_sim_args(xs, outs, ws, bits=4, tiles=tiles, out_dtype=oracle.OUT_BF16, ef=True,
+                               comps=comps)
+        echo.echo_allreduce_sim(a, streams=streams)
+        torch.cuda.synchronize()
+        # sampled parity against the oracle's own call on the mini message
+        o_outs, _, _ = oracle.allreduce(x_mini, bits=4, ef=True, comps=o_comps, out_dtype=oracle.OUT_BF16)
+        for r in range(P):
+            assert_bits_equal(host_u16(outs[r][idx]), o_outs[r], f"P={P} call {call} out[{r}] sample")
+            assert_bits_equal(host_f32(comps[r][idx]), o_comps[r], f"P={P} call {call} comp[{r}] sample")
+        # whole message: every rank holds the same bits
+        for r in range(1, P):
+            assert torch.equal(outs[r], outs[0]), f"rank {r} differs"
+        # whole message: out - sum(x + c) == sum(e) = -sum(comp after), chunked in fp64
+        step = 1 << 26
+        for a0 in range(0, n, step):
+            sl = slice(a0, a0 + step)
+            out = bf16_dev_to_f64(outs[0][sl])
+            u_sum = torch.zeros_like(out)
+            mag = torch.zeros_like(out)
+            e_sum = torch.zeros_like(out)
+            for r in range(P):
+                u = bf16_dev_to_f64(xs[r][sl])
+                if call == 1:
+                    u = u + c_before[r][sl].double()
+                u_sum += u
+                mag += u.abs()
+                e_sum -= comps[r][sl].double()
+            # the bf16 output rounding is part of what the owner's error cannot see
+            resid = (out - u_sum - e_sum).abs()
+            bound = (P + 2) * U24 * (mag + e_sum.abs() + out.abs()) + 2.0 ** -9 * out.abs()
+            assert bool((resid <= bound).all()), f"P={P} call {call} chunk {a0}: {resid.max().item()}"
+            del out, u_sum, mag, e_sum
+        del c_before
+    del xs, comps, outs, ws
+    torch.cuda.empty_cache()
+
+
+def chain_run(echo, P, n, hidden, sites, bits, gen, ef, slice_rows=16):
+    """Depth chain on the GPU with per-site oracle parity on a row slice."""
+    S = n // P
+    rows_per_seg = S // hidden
+    assert rows_per_seg >= slice_rows
+    idx = (torch.arange(P, device=DEV)[:, None] * S +
+           torch.arange(slice_rows * hidden, device=DEV)[None, :]).reshape(-1)
+    mini_n = idx.numel()
+    comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if ef else None
+    outs = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
+    o_comps = [np.zeros(mini_n, np.float32) for _ in range(P)] if ef else None
+    h = torch.zeros(n, dtype=torch.float64, device=DEV)
+    h_exact = torch.zeros(n, dtype=torch.float64, device=DEV)
+    rms = lambda t: float(torch.sqrt(torch.mean(t * t)))
+    E_rms, d_rms, debt_gap = [], [], []
+    for k in range(sites):
+        xs = [gen(r, k) for r in range(P)]
+        c_sum = sum(c.double() for c in comps) if ef else 0.0
+        a = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=4, out_dtype=oracle.OUT_F32, ef=ef, comps=comps)
+        echo.echo_allreduce_sim(a, streams=streams)
+        x_sum = sum(x.view(torch.bfloat16).double() for x in xs)
+        out = outs[0].double()
+        h += out
+        h_exact += x_sum
+        E = h - h_exact
+        E_rms.append(rms(E))
+        d_rms.append(rms(out - x_sum - c_sum))
+        if ef:
+            debt = -sum(c.double() for c in comps)
+            debt_gap.append(float((E - debt).abs().max()) / max(float(E.abs().max()), 1e-30))
+        # per-site parity on the slice
+        x_mini = [host_u16(x[idx]) for x in xs]
+        o_outs, _, _ = oracle.allreduce(x_mini, bits=bits, ef=ef, comps=o_comps, out_dtype=oracle.OUT_F32)
+        for r in range(P):
+            assert_bits_equal(host_f32(outs[r][idx]), o_outs[r], f"site {k} out[{r}] slice")
+        if ef:
+            for r in range(P):
+                assert_bits_equal(host_f32(comps[r][idx]), o_comps[r], f"site {k} comp[{r}] slice")
+        for r in range(1, P):
+            assert torch.equal(outs[r], outs[0])
+        del xs, x_sum, out, E
+    del comps, outs, ws, h, h_exact
+    torch.cuda.empty_cache()
+    return np.array(E_rms), np.array(d_rms), np.array(debt_gap)
+
+
+@pytest.mark.parametrize("which", ["chain", "chain8"])
+def test_depth_chain_bounded_with_feedback(echo, which):
+    if which == "chain":
+        P, tokens, hidden, sites, bits = 4, 2048, 4096, 64, 4
+        sigma = inputs.chain_channel_scale(hidden, device=DEV)
+        gen = lambda r, k: inputs.chain(r, k, tokens, hidden, sigma_h=sigma, device=DEV)
+    else:
+        P, tokens, hidden, sites, bits = 4, 4096, 1024, 56, 8
+        gen = lambda r, k: inputs.chain8(r, k, tokens, hidden, device=DEV)
+    n = tokens * hidden
+    say(which, "with feedback")
+    E_ef, d_ef, gap = chain_run(echo, P, n, hidden, sites, bits, gen, ef=True)
+    say(which, "without feedback")
+    E_off, d_off, _ = chain_run(echo, P, n, hidden, sites, bits, gen, ef=False)
+    print(f"{which}: max RMS E with EF {E_ef.max():.3e}, max RMS delta {d_ef.max():.3e}, "
+          f"RMS E_N without EF {E_off[-1]:.3e}, ratio {E_off[-1] / E_ef[-1]:.2f}, max debt gap {gap.max():.2e}",
+          flush=True)
+    # accumulated error == outstanding debt (fp32 rounding aside)
+    assert gap.max() < 1e-3
+    # bounded with feedback, independent of depth
+    assert E_ef.max() <= 1.25 * d_ef.max()
+    # accumulates without feedback
+    assert E_off[-1] >= 4.0 * E_ef[-1]
+    assert E_off[-1] > 1.5 * E_off[sites // 4]
