@@ -24,7 +24,10 @@ namespace {
 thread_local int t_last_hip_error = 0;
 
 constexpr int64_t kMaxN = int64_t(1) << 34;
-constexpr int kU = 2;  // groups per row per block (passes of 16 groups)
+#ifndef ECHO_U
+#define ECHO_U 2
+#endif
+constexpr int kU = ECHO_U;  // passes of 16 groups per block (groups per DPP row)
 
 int hip_fail(hipError_t e)
 {

@@ -46,6 +46,40 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- helpers --
 
+// Streaming accesses: every byte of the message is touched once per kernel,
+// so loads and stores of the big arrays may carry the non-temporal hint.
+#ifndef ECHO_NT
+#define ECHO_NT 1
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p)
+{
+    if constexpr (ECHO_NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, const T& v)
+{
+    if constexpr (ECHO_NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// fp32 streams (compensation in, error out) go through a wave-private LDS
+// slice so that every global fp32 access is lane-contiguous (1 KB per wave
+// instruction) while the arithmetic keeps 8 consecutive elements per lane.
+#ifndef ECHO_STAGE
+#define ECHO_STAGE 1
+#endif
+constexpr int kWaveChunk = 4 * kGroup;   // 512 elements: the 4 groups (rows) of one wave
+
+// orders this wave's LDS accesses across lanes (no block barrier needed: the
+// slice is private to the wave and the LDS executes a wave's operations in order)
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v)
 {
@@ -136,11 +170,11 @@ struct Packed<4> {
     }
     __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
     {
-        *(uint32_t*)(codes + (e0 >> 1)) = w;
+        st_stream((uint32_t*)(codes + (e0 >> 1)), w);
     }
     __device__ __forceinline__ void load(const uint8_t* codes, int64_t e0)
     {
-        w = *(const uint32_t*)(codes + (e0 >> 1));
+        w = ld_stream((const uint32_t*)(codes + (e0 >> 1)));
     }
     __device__ __forceinline__ void unpack(float* q) const
     {
@@ -158,11 +192,11 @@ struct Packed<8> {
     }
     __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
     {
-        *(u32x2*)(codes + e0) = w;
+        st_stream((u32x2*)(codes + e0), w);
     }
     __device__ __forceinline__ void load(const uint8_t* codes, int64_t e0)
     {
-        w = *(const u32x2*)(codes + e0);
+        w = ld_stream((const u32x2*)(codes + e0));
     }
     __device__ __forceinline__ void unpack(float* q) const
     {
@@ -174,11 +208,11 @@ struct Packed<8> {
 };
 
 // Quantize the lane's 8 values of one group (the whole row cooperates),
-// store codes and parameters, and optionally the error (q - z) * s - u.
+// store codes and parameters, and return the error (q - z) * s - u (or its
+// negation) in e.
 template <int BITS>
-__device__ __forceinline__ void quantize_store(const float* u, bool active, uint32_t l16, int64_t e0,
-                                               uint8_t* codes, uint32_t* params, float* err,
-                                               bool negate)
+__device__ __forceinline__ void quantize_row(const float* u, bool active, uint32_t l16, int64_t e0,
+                                             uint8_t* codes, uint32_t* params, bool negate, float* e)
 {
     float lo = 0.0f, hi = 0.0f;
 #pragma unroll
@@ -188,21 +222,53 @@ __device__ __forceinline__ void quantize_store(const float* u, bool active, uint
     float q[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = quant1<BITS>(u[i], p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = (q[i] - p.zf) * p.s - u[i];
+        e[i] = negate ? -v : v;
+    }
     if (!active) return;
     Packed<BITS> pk;
     pk.pack(q);
     pk.store(codes, e0);
     if (l16 == 0) params[e0 >> 7] = p.word;
-    if (err) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = (q[i] - p.zf) * p.s - u[i];
-            e[i] = negate ? -v : v;
-        }
-        *(f32x4*)(err + e0) = f32x4{e[0], e[1], e[2], e[3]};
-        *(f32x4*)(err + e0 + 4) = f32x4{e[4], e[5], e[6], e[7]};
+}
+
+// Where the lane-contiguous fp32 accesses of a wave land: half h (0/1) of the
+// wave's 512-element chunk covers rows 2h and 2h+1; lane l moves the float4 at
+// offset (4 l) mod 128 of row 2h + l/32.  Rows past the tile re-read the last
+// group (clamped) and are never stored.
+struct WaveMap {
+    int64_t seg0;          // first element of the tile in this segment
+    uint32_t gw;           // group index (within the tile) of the wave's row 0
+    uint32_t last;         // tile_groups - 1
+    uint32_t lane;
+    __device__ __forceinline__ uint32_t row_group(uint32_t r) const { return gw + r; }
+    __device__ __forceinline__ int64_t contig(uint32_t h) const
+    {
+        const uint32_t g = min(gw + 2u * h + (lane >> 5), last);
+        return seg0 + (int64_t)g * kGroup + (int64_t)((4u * lane) & (kGroup - 1));
     }
+    __device__ __forceinline__ bool contig_active(uint32_t h) const { return gw + 2u * h + (lane >> 5) <= last; }
+};
+
+// natural 8-float view of a lane <-> lane-contiguous float4 pairs, via LDS
+__device__ __forceinline__ void stage_in(float* slice, uint32_t lane, const f32x4& h0, const f32x4& h1)
+{
+    *(f32x4*)(slice + 4 * lane) = h0;
+    *(f32x4*)(slice + 256 + 4 * lane) = h1;
+}
+__device__ __forceinline__ void natural_read(const float* slice, uint32_t lane, float* v)
+{
+    const f32x4 a = *(const f32x4*)(slice + 8 * lane);
+    const f32x4 b = *(const f32x4*)(slice + 8 * lane + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void natural_write(float* slice, uint32_t lane, const float* v)
+{
+    *(f32x4*)(slice + 8 * lane) = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)(slice + 8 * lane + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
 // ------------------------------------------------------- push (entry pass) --
@@ -225,38 +291,86 @@ struct PushArgs {
 template <int BITS, int U>
 __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
 {
-    const uint32_t l16 = threadIdx.x & 15u;
-    const uint32_t row = threadIdx.x >> 4;
+    __shared__ float lds[ECHO_STAGE ? U * (kBlock / 64) * kWaveChunk : 1];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t l16 = lane & 15u;
+    const uint32_t rw = lane >> 4;                       // this lane's row in the wave
     const uint32_t si = blockIdx.y;
     const uint32_t seg = si + (si >= (uint32_t)a.rank ? 1u : 0u);
     const int64_t seg0 = (int64_t)seg * a.S + a.tile_begin;
-    const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
+    const uint32_t last = a.tile_groups - 1u;
+    const bool has_comp = a.comp != nullptr;
+    const bool has_err = a.err != nullptr;
 
+    WaveMap wm[U];
     u32x4 xv[U];
     f32x4 c0[U], c1[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_groups - 1u);
-        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
-        xv[k] = *(const u32x4*)(a.x + e0);
-        if (a.comp) {
-            c0[k] = *(const f32x4*)(a.comp + e0);
-            c1[k] = *(const f32x4*)(a.comp + e0 + 4);
+        wm[k].seg0 = seg0;
+        wm[k].gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
+        wm[k].last = last;
+        wm[k].lane = lane;
+        const int64_t e0 = seg0 + (int64_t)min(wm[k].row_group(rw), last) * kGroup + (int64_t)(l16 * kEPL);
+        xv[k] = ld_stream((const u32x4*)(a.x + e0));
+        if (has_comp) {
+            if (ECHO_STAGE) {
+                c0[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(0)));
+                c1[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(1)));
+            } else {
+                c0[k] = ld_stream((const f32x4*)(a.comp + e0));
+                c1[k] = ld_stream((const f32x4*)(a.comp + e0 + 4));
+            }
         }
+    }
+    float* slice0 = lds + wave * kWaveChunk;
+    if (ECHO_STAGE && has_comp) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) stage_in(slice0 + k * (kBlock / 64) * kWaveChunk, lane, c0[k], c1[k]);
+        wave_lds_fence();
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
-        const bool active = graw < a.tile_groups;
-        const uint32_t gi = min(graw, a.tile_groups - 1u);
-        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
+        const uint32_t graw = wm[k].row_group(rw);
+        const bool active = graw <= last;
+        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kGroup + (int64_t)(l16 * kEPL);
         float u[8];
         unpack_bf16x8(xv[k], u);
-        if (a.comp) {
-            u[0] += c0[k].x; u[1] += c0[k].y; u[2] += c0[k].z; u[3] += c0[k].w;
-            u[4] += c1[k].x; u[5] += c1[k].y; u[6] += c1[k].z; u[7] += c1[k].w;
+        if (has_comp) {
+            float c[8];
+            if (ECHO_STAGE) {
+                natural_read(slice, lane, c);
+            } else {
+                c[0] = c0[k].x; c[1] = c0[k].y; c[2] = c0[k].z; c[3] = c0[k].w;
+                c[4] = c1[k].x; c[5] = c1[k].y; c[6] = c1[k].z; c[7] = c1[k].w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] += c[i];
         }
-        quantize_store<BITS>(u, active, l16, e0, a.codes, a.params, a.err, a.negate != 0);
+        float e[8];
+        quantize_row<BITS>(u, active, l16, e0, a.codes, a.params, a.negate != 0, e);
+        if (has_err) {
+            if (ECHO_STAGE) {
+                natural_write(slice, lane, e);
+            } else if (active) {
+                st_stream((f32x4*)(a.err + e0), f32x4{e[0], e[1], e[2], e[3]});
+                st_stream((f32x4*)(a.err + e0 + 4), f32x4{e[4], e[5], e[6], e[7]});
+            }
+        }
+    }
+    if (ECHO_STAGE && has_err) {
+        wave_lds_fence();
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
+#pragma unroll
+            for (uint32_t h = 0; h < 2; ++h) {
+                const f32x4 v = *(const f32x4*)(slice + 256 * h + 4 * lane);
+                if (wm[k].contig_active(h)) st_stream((f32x4*)(a.err + wm[k].contig(h)), v);
+            }
+        }
     }
 }
 
@@ -281,23 +395,37 @@ struct ReduceArgs {
 template <int BITS, int P, int U>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
 {
-    const uint32_t l16 = threadIdx.x & 15u;
-    const uint32_t row = threadIdx.x >> 4;
+    __shared__ float lds[ECHO_STAGE ? U * (kBlock / 64) * kWaveChunk : 1];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t l16 = lane & 15u;
+    const uint32_t rw = lane >> 4;
     const int64_t seg0 = (int64_t)a.owner * a.S + a.tile_begin;
-    const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
+    const uint32_t last = a.tile_groups - 1u;
+    const bool has_comp = a.comp != nullptr;
+    const bool has_err = a.err != nullptr;
 
+    WaveMap wm[U];
     u32x4 xv[U];
     f32x4 c0[U], c1[U];
     Packed<BITS> pk[U][P];
     uint32_t pw[U][P];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_groups - 1u);
-        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
-        xv[k] = *(const u32x4*)(a.x + e0);
-        if (a.comp) {
-            c0[k] = *(const f32x4*)(a.comp + e0);
-            c1[k] = *(const f32x4*)(a.comp + e0 + 4);
+        wm[k].seg0 = seg0;
+        wm[k].gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
+        wm[k].last = last;
+        wm[k].lane = lane;
+        const int64_t e0 = seg0 + (int64_t)min(wm[k].row_group(rw), last) * kGroup + (int64_t)(l16 * kEPL);
+        xv[k] = ld_stream((const u32x4*)(a.x + e0));
+        if (has_comp) {
+            if (ECHO_STAGE) {
+                c0[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(0)));
+                c1[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(1)));
+            } else {
+                c0[k] = ld_stream((const f32x4*)(a.comp + e0));
+                c1[k] = ld_stream((const f32x4*)(a.comp + e0 + 4));
+            }
         }
 #pragma unroll
         for (int j = 0; j < P; ++j) {
@@ -307,17 +435,30 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
             }
         }
     }
+    float* slice0 = lds + wave * kWaveChunk;
+    if (ECHO_STAGE && has_comp) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) stage_in(slice0 + k * (kBlock / 64) * kWaveChunk, lane, c0[k], c1[k]);
+        wave_lds_fence();
+    }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
-        const bool active = graw < a.tile_groups;
-        const uint32_t gi = min(graw, a.tile_groups - 1u);
-        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
+        const uint32_t graw = wm[k].row_group(rw);
+        const bool active = graw <= last;
+        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kGroup + (int64_t)(l16 * kEPL);
         float own[8];
         unpack_bf16x8(xv[k], own);
-        if (a.comp) {
-            own[0] += c0[k].x; own[1] += c0[k].y; own[2] += c0[k].z; own[3] += c0[k].w;
-            own[4] += c1[k].x; own[5] += c1[k].y; own[6] += c1[k].z; own[7] += c1[k].w;
+        if (has_comp) {
+            float c[8];
+            if (ECHO_STAGE) {
+                natural_read(slice, lane, c);
+            } else {
+                c[0] = c0[k].x; c[1] = c0[k].y; c[2] = c0[k].z; c[3] = c0[k].w;
+                c[4] = c1[k].x; c[5] = c1[k].y; c[6] = c1[k].z; c[7] = c1[k].w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) own[i] += c[i];
         }
         // fp32 sum in rank order; the owner's own term enters unquantized
         float acc[8];
@@ -343,7 +484,28 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
                 for (int i = 0; i < 8; ++i) acc[i] = acc[i] + t[i];
             }
         }
-        quantize_store<BITS>(acc, active, l16, e0, a.sc, a.sp, a.err, a.negate != 0);
+        float e[8];
+        quantize_row<BITS>(acc, active, l16, e0, a.sc, a.sp, a.negate != 0, e);
+        if (has_err) {
+            if (ECHO_STAGE) {
+                natural_write(slice, lane, e);
+            } else if (active) {
+                st_stream((f32x4*)(a.err + e0), f32x4{e[0], e[1], e[2], e[3]});
+                st_stream((f32x4*)(a.err + e0 + 4), f32x4{e[4], e[5], e[6], e[7]});
+            }
+        }
+    }
+    if (ECHO_STAGE && has_err) {
+        wave_lds_fence();
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
+#pragma unroll
+            for (uint32_t h = 0; h < 2; ++h) {
+                const f32x4 v = *(const f32x4*)(slice + 256 * h + 4 * lane);
+                if (wm[k].contig_active(h)) st_stream((f32x4*)(a.err + wm[k].contig(h)), v);
+            }
+        }
     }
 }
 
@@ -393,11 +555,11 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
             w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
             w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
             w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
-            *(u32x4*)((uint16_t*)a.out + e0) = w;
+            st_stream((u32x4*)((uint16_t*)a.out + e0), w);
         } else {
             float* o = (float*)a.out + e0;
-            *(f32x4*)o = f32x4{v[0], v[1], v[2], v[3]};
-            *(f32x4*)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            st_stream((f32x4*)o, f32x4{v[0], v[1], v[2], v[3]});
+            st_stream((f32x4*)(o + 4), f32x4{v[4], v[5], v[6], v[7]});
         }
     }
 }

@@ -107,18 +107,27 @@ def training(rank: int, step: int, site: int, backward: bool, n: int,
 
 def laplace(rank: int, n: int, device="cpu", chunk: int = 1 << 26, workload: str = "onegb") -> torch.Tensor:
     """Laplace(0, 1) by inversion of a uniform draw, generated in chunks so
-    that the float32 temporaries stay small next to a 1 GiB output.  |u| is
-    kept below 1/2 (a draw of exactly 0 would give log(0) = -inf), which caps
-    |x| at about 17.3."""
+    that the float32 temporaries stay small next to a 1 GiB output.  |u - 1/2|
+    is kept below 1/2 (a draw of exactly 0 would give log(0) = -inf), which caps
+    |x| at 24*ln 2 = 16.6."""
     g = _gen(seed_of(workload, 0, 0, rank), device=device)
     out = torch.empty(n, dtype=torch.int16, device=device)
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
-        u = torch.rand(b - a, generator=g, dtype=torch.float32, device=device) - 0.5
-        x = -torch.sign(u) * torch.log1p(-2.0 * u.abs().clamp(max=0.5 - 2.0 ** -26))
-        out[a:b] = _bf16_bits(x)
-        del u, x
+        u = torch.rand(b - a, generator=g, dtype=torch.float32, device=device)
+        out[a:b] = _bf16_bits(laplace_from_uniform(u))
+        del u
     return out
+
+
+# the largest float32 below 1/2 (0.5 - 2^-26 would round back to 0.5)
+_HALF_BELOW = 0.5 - 2.0 ** -25
+
+
+def laplace_from_uniform(u: torch.Tensor) -> torch.Tensor:
+    """Laplace(0, 1) from U[0, 1) draws by inversion, finite for every draw."""
+    c = u - 0.5
+    return -torch.sign(c) * torch.log1p(-2.0 * c.abs().clamp(max=_HALF_BELOW))
 
 
 def as_numpy_u16(t: torch.Tensor):
