@@ -75,39 +75,61 @@ unsigned blocks_for(uint32_t tile_groups) { return (tile_groups + echo::kRowsPer
 // ---------------------------------------------------------------- launchers --
 // Each assumes validated arguments and tile_len > 0.
 
+echo::UpdArgs make_upd(float* slow, float alpha, float beta)
+{
+    echo::UpdArgs u;
+    u.slow = slow;
+    u.alpha = alpha;
+    u.beta = beta;
+    u.one_minus_alpha = 1.0f - alpha;
+    u.one_minus_beta = 1.0f - beta;
+    return u;
+}
+
+// upd != nullptr: fused two-timescale update (comp and upd->slow in place, err unused)
 int launch_push(const uint16_t* x, const float* comp, int64_t n, int P, int rank, int64_t tb,
                 int64_t tl, int bits, uint8_t* codes, echo_qparam* params, float* err, int flags,
-                hipStream_t st)
+                const echo::UpdArgs* upd, hipStream_t st)
 {
     if (P == 1) return ECHO_OK;   // a single rank owns everything: nothing to push
     echo::PushArgs a;
+    std::memset(&a, 0, sizeof(a));
     a.x = x; a.comp = comp; a.codes = codes; a.params = (uint32_t*)params; a.err = err;
     a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
     a.rank = rank; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    if (upd) a.upd = *upd;
     dim3 grid(blocks_for(a.tile_groups), (unsigned)(P - 1));
-    if (bits == 4) hipLaunchKernelGGL((echo::push_kernel<4, kU>), grid, dim3(echo::kBlock), 0, st, a);
-    else hipLaunchKernelGGL((echo::push_kernel<8, kU>), grid, dim3(echo::kBlock), 0, st, a);
+    dim3 block(echo::kBlock);
+    if (bits == 4) {
+        if (upd) hipLaunchKernelGGL((echo::push_kernel<4, kU, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((echo::push_kernel<4, kU, false>), grid, block, 0, st, a);
+    } else {
+        if (upd) hipLaunchKernelGGL((echo::push_kernel<8, kU, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((echo::push_kernel<8, kU, false>), grid, block, 0, st, a);
+    }
     return check_launch();
 }
 
-template <int BITS>
+template <int BITS, bool UPD>
 void launch_reduce_p(const echo::ReduceArgs& a, int P, dim3 grid, hipStream_t st)
 {
+    dim3 block(echo::kBlock);
     switch (P) {
-    case 1: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 1, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 2, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 3, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 4, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    case 5: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 5, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 6, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    case 7: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 7, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
-    default: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 8, kU>), grid, dim3(echo::kBlock), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 1, kU, UPD>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 2, kU, UPD>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 3, kU, UPD>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 4, kU, UPD>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 5, kU, UPD>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 6, kU, UPD>), grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 7, kU, UPD>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 8, kU, UPD>), grid, block, 0, st, a); break;
     }
 }
 
 int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc,
                   const echo_qparam* const* pp, int P, int owner, int64_t n, int64_t tb, int64_t tl,
-                  int bits, uint8_t* sc, echo_qparam* sp, float* err, int flags, hipStream_t st)
+                  int bits, uint8_t* sc, echo_qparam* sp, float* err, int flags,
+                  const echo::UpdArgs* upd, hipStream_t st)
 {
     echo::ReduceArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -119,9 +141,15 @@ int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc
     a.sc = sc; a.sp = (uint32_t*)sp; a.err = err;
     a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
     a.owner = owner; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    if (upd) a.upd = *upd;
     dim3 grid(blocks_for(a.tile_groups), 1);
-    if (bits == 4) launch_reduce_p<4>(a, P, grid, st);
-    else launch_reduce_p<8>(a, P, grid, st);
+    if (bits == 4) {
+        if (upd) launch_reduce_p<4, true>(a, P, grid, st);
+        else launch_reduce_p<4, false>(a, P, grid, st);
+    } else {
+        if (upd) launch_reduce_p<8, true>(a, P, grid, st);
+        else launch_reduce_p<8, false>(a, P, grid, st);
+    }
     return check_launch();
 }
 
@@ -148,10 +176,8 @@ int launch_compensate(const float* err, float* comp, float* slow, int64_t n, flo
 {
     if (n == 0) return ECHO_OK;
     echo::CompArgs a;
-    a.err = err; a.comp = comp; a.slow = slow; a.n = n;
-    a.alpha = alpha; a.beta = beta;
-    a.one_minus_alpha = 1.0f - alpha;
-    a.one_minus_beta = 1.0f - beta;
+    a.err = err; a.comp = comp; a.n = n;
+    a.upd = make_upd(slow, alpha, beta);
     int64_t chunks = (n + 3) / 4;
     int64_t blocks = (chunks + echo::kBlock - 1) / echo::kBlock;
     if (blocks > 8192) blocks = 8192;
@@ -246,7 +272,7 @@ int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P
         (comp && !aligned16(comp)) || (err && !aligned16(err)))
         return ECHO_EALIGN;
     return launch_push(x_bf16, comp, n, P, rank, tile_begin, tile_len, bits, codes, params, err, flags,
-                       (hipStream_t)stream);
+                       nullptr, (hipStream_t)stream);
 }
 
 int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
@@ -271,7 +297,7 @@ int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
         (own_comp && !aligned16(own_comp)) || (own_err && !aligned16(own_err)))
         return ECHO_EALIGN;
     return launch_reduce(own_x_bf16, own_comp, peer_codes, peer_params, P, owner, n, tile_begin, tile_len,
-                         bits, sum_codes, sum_params, own_err, flags, (hipStream_t)stream);
+                         bits, sum_codes, sum_params, own_err, flags, nullptr, (hipStream_t)stream);
 }
 
 int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params, int64_t n,
@@ -329,7 +355,6 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         }
         if (any_err && !all_err) return ECHO_EINVAL;
         fused = !any_err;
-        if (fused && !(a->alpha == 1.0f && a->beta == 0.0f)) return ECHO_EINVAL;
         bool slow_all = true, slow_any = false;
         for (int r = 0; r < P; ++r) {
             slow_all = slow_all && a->slow[r] != nullptr;
@@ -399,7 +424,13 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
                 return hip_fail(he);
     }
 
-    const int flags = fused ? ECHO_ERR_NEGATED : 0;
+    // feedback forms: classic fused (-e written into comp), two-timescale
+    // fused (comp and slow updated in the kernels), or unfused (e into err,
+    // then echo_compensate after the last reduce)
+    const bool two_fused = a->ef && fused && a->beta > 0.0f;
+    const int flags = (fused && !two_fused) ? ECHO_ERR_NEGATED : 0;
+    echo::UpdArgs upd_r[ECHO_MAX_P];
+    for (int r = 0; r < P; ++r) upd_r[r] = make_upd(a->slow[r], a->alpha, a->beta);
     for (int64_t t = 0; t < T; ++t) {
         const int64_t tb = t * tile_len;
         const int64_t tl = (tb + tile_len <= S) ? tile_len : S - tb;
@@ -407,8 +438,8 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         for (int r = 0; r < P; ++r) {
             const float* c = a->ef ? a->comp[r] : nullptr;
             float* e = a->ef ? (fused ? a->comp[r] : a->err[r]) : nullptr;
-            rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, (uint8_t*)pc[r], (echo_qparam*)pp[r], e,
-                             flags, s_push);
+            rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, (uint8_t*)pc[r], (echo_qparam*)pp[r],
+                             two_fused ? nullptr : e, flags, two_fused ? &upd_r[r] : nullptr, s_push);
             if (rc) return rc;
         }
         if (multi) {
@@ -419,7 +450,8 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         for (int o = 0; o < P; ++o) {
             const float* c = a->ef ? a->comp[o] : nullptr;
             float* e = a->ef ? (fused ? a->comp[o] : a->err[o]) : nullptr;
-            rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, sc, sp, e, flags, s_red);
+            rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, sc, sp, two_fused ? nullptr : e,
+                               flags, two_fused ? &upd_r[o] : nullptr, s_red);
             if (rc) return rc;
         }
         if (multi) {

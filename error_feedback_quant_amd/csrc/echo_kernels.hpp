@@ -271,7 +271,120 @@ __device__ __forceinline__ void natural_write(float* slice, uint32_t lane, const
     *(f32x4*)(slice + 8 * lane + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+// ------------------------------------------- fp32 stream I/O of a wavefront --
+// Loads the compensation (and, for UPD, the slow memory) of U passes, and
+// writes back either the error (err) or the updated compensation and slow
+// memory, lane-contiguously through the wave's LDS slices when staging.
+
+template <int U, bool UPD>
+struct Fp32Io {
+    static constexpr int kSlices = UPD ? 2 : 1;
+    static constexpr int kPassStride = (kBlock / 64) * kWaveChunk;       // floats per pass (4 waves)
+    static constexpr int kLdsFloats = ECHO_STAGE ? U * kSlices * kPassStride : 1;
+
+    f32x4 c0[U], c1[U], m0[U], m1[U];
+
+    __device__ __forceinline__ static float* slice(float* lds, int k, int which, uint32_t wave)
+    {
+        return lds + (k * kSlices + which) * kPassStride + wave * kWaveChunk;
+    }
+
+    __device__ __forceinline__ void load(int k, const WaveMap& wm, int64_t e0, const float* comp,
+                                         const float* slow)
+    {
+        if (ECHO_STAGE) {
+            c0[k] = ld_stream((const f32x4*)(comp + wm.contig(0)));
+            c1[k] = ld_stream((const f32x4*)(comp + wm.contig(1)));
+            if (UPD) {
+                m0[k] = ld_stream((const f32x4*)(slow + wm.contig(0)));
+                m1[k] = ld_stream((const f32x4*)(slow + wm.contig(1)));
+            }
+        } else {
+            c0[k] = ld_stream((const f32x4*)(comp + e0));
+            c1[k] = ld_stream((const f32x4*)(comp + e0 + 4));
+            if (UPD) {
+                m0[k] = ld_stream((const f32x4*)(slow + e0));
+                m1[k] = ld_stream((const f32x4*)(slow + e0 + 4));
+            }
+        }
+    }
+
+    __device__ __forceinline__ void stage(float* lds, uint32_t wave, uint32_t lane)
+    {
+        if (!ECHO_STAGE) return;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            stage_in(slice(lds, k, 0, wave), lane, c0[k], c1[k]);
+            if (UPD) stage_in(slice(lds, k, 1, wave), lane, m0[k], m1[k]);
+        }
+        wave_lds_fence();
+    }
+
+    // the lane's 8 natural values of pass k (which = 0: comp, 1: slow)
+    __device__ __forceinline__ void natural(float* lds, int k, int which, uint32_t wave, uint32_t lane, float* v) const
+    {
+        if (ECHO_STAGE) {
+            natural_read(slice(lds, k, which, wave), lane, v);
+        } else {
+            const f32x4& a = which ? m0[k] : c0[k];
+            const f32x4& b = which ? m1[k] : c1[k];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+    }
+
+    // stage the 8 natural outputs of pass k for slice `which`, or store them
+    // directly when not staging
+    __device__ __forceinline__ void put(float* lds, int k, int which, uint32_t wave, uint32_t lane,
+                                        const float* v, bool active, float* dst, int64_t e0)
+    {
+        if (ECHO_STAGE) {
+            natural_write(slice(lds, k, which, wave), lane, v);
+        } else if (active) {
+            st_stream((f32x4*)(dst + e0), f32x4{v[0], v[1], v[2], v[3]});
+            st_stream((f32x4*)(dst + e0 + 4), f32x4{v[4], v[5], v[6], v[7]});
+        }
+    }
+
+    // after all passes: the staged outputs go out lane-contiguously
+    __device__ __forceinline__ void flush(float* lds, uint32_t wave, uint32_t lane, const WaveMap* wm,
+                                          float* dst0, float* dst1)
+    {
+        if (!ECHO_STAGE) return;
+        wave_lds_fence();
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+#pragma unroll
+            for (uint32_t h = 0; h < 2; ++h) {
+                if (!wm[k].contig_active(h)) continue;
+                const int64_t g = wm[k].contig(h);
+                st_stream((f32x4*)(dst0 + g), *(const f32x4*)(slice(lds, k, 0, wave) + 256 * h + 4 * lane));
+                if (UPD) st_stream((f32x4*)(dst1 + g), *(const f32x4*)(slice(lds, k, 1, wave) + 256 * h + 4 * lane));
+            }
+        }
+    }
+};
+
 // ------------------------------------------------------- push (entry pass) --
+
+// Fused two-timescale update (UPD kernels): instead of writing e, the kernel
+// applies c' = -(alpha*e + beta*M), M' = (1-beta)*M + (1-alpha)*e in place on
+// the compensation and slow-memory buffers -- the same IEEE operations, in the
+// same order, as compensate_kernel, so the results are bit-identical.
+struct UpdArgs {
+    float* slow;
+    float alpha, beta, one_minus_alpha, one_minus_beta;
+};
+
+__device__ __forceinline__ void update1(const UpdArgs& a, float e, float m, float& c_out, float& m_out)
+{
+    const float fa = a.alpha * e;
+    const float fb = a.beta * m;
+    c_out = -(fa + fb);
+    const float m1 = a.one_minus_beta * m;
+    const float m2 = a.one_minus_alpha * e;
+    m_out = m1 + m2;
+}
 
 struct PushArgs {
     const uint16_t* x;
@@ -284,14 +397,17 @@ struct PushArgs {
     uint32_t tile_groups;   // groups per segment tile (>= 1)
     int rank;
     int negate;
+    UpdArgs upd;            // UPD kernels only: comp is updated in place
 };
 
 // grid: (ceil(tile_groups / (16 U)), P - 1); blockIdx.y = index among the
-// segments this rank does not own.
-template <int BITS, int U>
+// segments this rank does not own.  UPD: comp and upd.slow are required and
+// updated in place (err unused).
+template <int BITS, int U, bool UPD>
 __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
 {
-    __shared__ float lds[ECHO_STAGE ? U * (kBlock / 64) * kWaveChunk : 1];
+    using Io = Fp32Io<U, UPD>;
+    __shared__ float lds[Io::kLdsFloats];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = lane & 15u;
@@ -300,12 +416,12 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
     const uint32_t seg = si + (si >= (uint32_t)a.rank ? 1u : 0u);
     const int64_t seg0 = (int64_t)seg * a.S + a.tile_begin;
     const uint32_t last = a.tile_groups - 1u;
-    const bool has_comp = a.comp != nullptr;
-    const bool has_err = a.err != nullptr;
+    const bool has_comp = UPD || a.comp != nullptr;
+    const bool has_out = UPD || a.err != nullptr;
 
     WaveMap wm[U];
     u32x4 xv[U];
-    f32x4 c0[U], c1[U];
+    Io io;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         wm[k].seg0 = seg0;
@@ -314,25 +430,11 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
         wm[k].lane = lane;
         const int64_t e0 = seg0 + (int64_t)min(wm[k].row_group(rw), last) * kGroup + (int64_t)(l16 * kEPL);
         xv[k] = ld_stream((const u32x4*)(a.x + e0));
-        if (has_comp) {
-            if (ECHO_STAGE) {
-                c0[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(0)));
-                c1[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(1)));
-            } else {
-                c0[k] = ld_stream((const f32x4*)(a.comp + e0));
-                c1[k] = ld_stream((const f32x4*)(a.comp + e0 + 4));
-            }
-        }
+        if (has_comp) io.load(k, wm[k], e0, a.comp, a.upd.slow);
     }
-    float* slice0 = lds + wave * kWaveChunk;
-    if (ECHO_STAGE && has_comp) {
-#pragma unroll
-        for (int k = 0; k < U; ++k) stage_in(slice0 + k * (kBlock / 64) * kWaveChunk, lane, c0[k], c1[k]);
-        wave_lds_fence();
-    }
+    if (has_comp) io.stage(lds, wave, lane);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
         const uint32_t graw = wm[k].row_group(rw);
         const bool active = graw <= last;
         const int64_t e0 = seg0 + (int64_t)min(graw, last) * kGroup + (int64_t)(l16 * kEPL);
@@ -340,38 +442,24 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
         unpack_bf16x8(xv[k], u);
         if (has_comp) {
             float c[8];
-            if (ECHO_STAGE) {
-                natural_read(slice, lane, c);
-            } else {
-                c[0] = c0[k].x; c[1] = c0[k].y; c[2] = c0[k].z; c[3] = c0[k].w;
-                c[4] = c1[k].x; c[5] = c1[k].y; c[6] = c1[k].z; c[7] = c1[k].w;
-            }
+            io.natural(lds, k, 0, wave, lane, c);
 #pragma unroll
             for (int i = 0; i < 8; ++i) u[i] += c[i];
         }
         float e[8];
-        quantize_row<BITS>(u, active, l16, e0, a.codes, a.params, a.negate != 0, e);
-        if (has_err) {
-            if (ECHO_STAGE) {
-                natural_write(slice, lane, e);
-            } else if (active) {
-                st_stream((f32x4*)(a.err + e0), f32x4{e[0], e[1], e[2], e[3]});
-                st_stream((f32x4*)(a.err + e0 + 4), f32x4{e[4], e[5], e[6], e[7]});
-            }
+        quantize_row<BITS>(u, active, l16, e0, a.codes, a.params, UPD ? false : a.negate != 0, e);
+        if (UPD) {
+            float m[8], cn[8], mn[8];
+            io.natural(lds, k, 1, wave, lane, m);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) update1(a.upd, e[i], m[i], cn[i], mn[i]);
+            io.put(lds, k, 0, wave, lane, cn, active, (float*)a.comp, e0);
+            io.put(lds, k, 1, wave, lane, mn, active, a.upd.slow, e0);
+        } else if (has_out) {
+            io.put(lds, k, 0, wave, lane, e, active, a.err, e0);
         }
     }
-    if (ECHO_STAGE && has_err) {
-        wave_lds_fence();
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
-#pragma unroll
-            for (uint32_t h = 0; h < 2; ++h) {
-                const f32x4 v = *(const f32x4*)(slice + 256 * h + 4 * lane);
-                if (wm[k].contig_active(h)) st_stream((f32x4*)(a.err + wm[k].contig(h)), v);
-            }
-        }
-    }
+    if (has_out) io.flush(lds, wave, lane, wm, UPD ? (float*)a.comp : a.err, a.upd.slow);
 }
 
 // ------------------------------------------------------------ owner reduce --
@@ -389,25 +477,27 @@ struct ReduceArgs {
     uint32_t tile_groups;
     int owner;
     int negate;
+    UpdArgs upd;                    // UPD kernels only
 };
 
-// grid: (ceil(tile_groups / (16 U)), 1)
-template <int BITS, int P, int U>
+// grid: (ceil(tile_groups / (16 U)), 1).  UPD as for push_kernel.
+template <int BITS, int P, int U, bool UPD>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
 {
-    __shared__ float lds[ECHO_STAGE ? U * (kBlock / 64) * kWaveChunk : 1];
+    using Io = Fp32Io<U, UPD>;
+    __shared__ float lds[Io::kLdsFloats];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = lane & 15u;
     const uint32_t rw = lane >> 4;
     const int64_t seg0 = (int64_t)a.owner * a.S + a.tile_begin;
     const uint32_t last = a.tile_groups - 1u;
-    const bool has_comp = a.comp != nullptr;
-    const bool has_err = a.err != nullptr;
+    const bool has_comp = UPD || a.comp != nullptr;
+    const bool has_out = UPD || a.err != nullptr;
 
     WaveMap wm[U];
     u32x4 xv[U];
-    f32x4 c0[U], c1[U];
+    Io io;
     Packed<BITS> pk[U][P];
     uint32_t pw[U][P];
 #pragma unroll
@@ -418,15 +508,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
         wm[k].lane = lane;
         const int64_t e0 = seg0 + (int64_t)min(wm[k].row_group(rw), last) * kGroup + (int64_t)(l16 * kEPL);
         xv[k] = ld_stream((const u32x4*)(a.x + e0));
-        if (has_comp) {
-            if (ECHO_STAGE) {
-                c0[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(0)));
-                c1[k] = ld_stream((const f32x4*)(a.comp + wm[k].contig(1)));
-            } else {
-                c0[k] = ld_stream((const f32x4*)(a.comp + e0));
-                c1[k] = ld_stream((const f32x4*)(a.comp + e0 + 4));
-            }
-        }
+        if (has_comp) io.load(k, wm[k], e0, a.comp, a.upd.slow);
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             if (j != a.owner) {
@@ -435,15 +517,9 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
             }
         }
     }
-    float* slice0 = lds + wave * kWaveChunk;
-    if (ECHO_STAGE && has_comp) {
-#pragma unroll
-        for (int k = 0; k < U; ++k) stage_in(slice0 + k * (kBlock / 64) * kWaveChunk, lane, c0[k], c1[k]);
-        wave_lds_fence();
-    }
+    if (has_comp) io.stage(lds, wave, lane);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
         const uint32_t graw = wm[k].row_group(rw);
         const bool active = graw <= last;
         const int64_t e0 = seg0 + (int64_t)min(graw, last) * kGroup + (int64_t)(l16 * kEPL);
@@ -451,12 +527,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
         unpack_bf16x8(xv[k], own);
         if (has_comp) {
             float c[8];
-            if (ECHO_STAGE) {
-                natural_read(slice, lane, c);
-            } else {
-                c[0] = c0[k].x; c[1] = c0[k].y; c[2] = c0[k].z; c[3] = c0[k].w;
-                c[4] = c1[k].x; c[5] = c1[k].y; c[6] = c1[k].z; c[7] = c1[k].w;
-            }
+            io.natural(lds, k, 0, wave, lane, c);
 #pragma unroll
             for (int i = 0; i < 8; ++i) own[i] += c[i];
         }
@@ -485,28 +556,19 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
             }
         }
         float e[8];
-        quantize_row<BITS>(acc, active, l16, e0, a.sc, a.sp, a.negate != 0, e);
-        if (has_err) {
-            if (ECHO_STAGE) {
-                natural_write(slice, lane, e);
-            } else if (active) {
-                st_stream((f32x4*)(a.err + e0), f32x4{e[0], e[1], e[2], e[3]});
-                st_stream((f32x4*)(a.err + e0 + 4), f32x4{e[4], e[5], e[6], e[7]});
-            }
+        quantize_row<BITS>(acc, active, l16, e0, a.sc, a.sp, UPD ? false : a.negate != 0, e);
+        if (UPD) {
+            float m[8], cn[8], mn[8];
+            io.natural(lds, k, 1, wave, lane, m);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) update1(a.upd, e[i], m[i], cn[i], mn[i]);
+            io.put(lds, k, 0, wave, lane, cn, active, (float*)a.comp, e0);
+            io.put(lds, k, 1, wave, lane, mn, active, a.upd.slow, e0);
+        } else if (has_out) {
+            io.put(lds, k, 0, wave, lane, e, active, a.err, e0);
         }
     }
-    if (ECHO_STAGE && has_err) {
-        wave_lds_fence();
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const float* slice = slice0 + k * (kBlock / 64) * kWaveChunk;
-#pragma unroll
-            for (uint32_t h = 0; h < 2; ++h) {
-                const f32x4 v = *(const f32x4*)(slice + 256 * h + 4 * lane);
-                if (wm[k].contig_active(h)) st_stream((f32x4*)(a.err + wm[k].contig(h)), v);
-            }
-        }
-    }
+    if (has_out) io.flush(lds, wave, lane, wm, UPD ? (float*)a.comp : a.err, a.upd.slow);
 }
 
 // ------------------------------------------------------ gather / tail decode --
@@ -569,43 +631,33 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 struct CompArgs {
     const float* err;
     float* comp;
-    float* slow;        // nullable (beta == 0)
     int64_t n;
-    float alpha, beta, one_minus_alpha, one_minus_beta;
+    UpdArgs upd;        // upd.slow nullable (beta == 0)
 };
 
-__device__ __forceinline__ void comp1(const CompArgs& a, float e, float m, float& c_out, float& m_out)
-{
-    const float fa = a.alpha * e;
-    const float fb = a.beta * m;
-    c_out = -(fa + fb);
-    const float m1 = a.one_minus_beta * m;
-    const float m2 = a.one_minus_alpha * e;
-    m_out = m1 + m2;
-}
-
-// grid-stride over float4 chunks, then a scalar tail
+// grid-stride over float4 chunks, then a scalar tail.  Without a slow memory
+// (beta == 0) the update is c' = -(alpha*e).
 template <bool SLOW>
 __global__ __launch_bounds__(kBlock) void compensate_kernel(const CompArgs a)
 {
     const int64_t n4 = a.n >> 2;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) {
-        const f32x4 e = *(const f32x4*)(a.err + 4 * i);
+        const f32x4 e = ld_stream((const f32x4*)(a.err + 4 * i));
         float c[4];
         if (SLOW) {
-            const f32x4 m = *(const f32x4*)(a.slow + 4 * i);
+            const f32x4 m = ld_stream((const f32x4*)(a.upd.slow + 4 * i));
             float mo[4];
-            comp1(a, e.x, m.x, c[0], mo[0]);
-            comp1(a, e.y, m.y, c[1], mo[1]);
-            comp1(a, e.z, m.z, c[2], mo[2]);
-            comp1(a, e.w, m.w, c[3], mo[3]);
-            *(f32x4*)(a.slow + 4 * i) = f32x4{mo[0], mo[1], mo[2], mo[3]};
+            update1(a.upd, e.x, m.x, c[0], mo[0]);
+            update1(a.upd, e.y, m.y, c[1], mo[1]);
+            update1(a.upd, e.z, m.z, c[2], mo[2]);
+            update1(a.upd, e.w, m.w, c[3], mo[3]);
+            st_stream((f32x4*)(a.upd.slow + 4 * i), f32x4{mo[0], mo[1], mo[2], mo[3]});
         } else {
-            c[0] = -(a.alpha * e.x); c[1] = -(a.alpha * e.y);
-            c[2] = -(a.alpha * e.z); c[3] = -(a.alpha * e.w);
+            c[0] = -(a.upd.alpha * e.x); c[1] = -(a.upd.alpha * e.y);
+            c[2] = -(a.upd.alpha * e.z); c[3] = -(a.upd.alpha * e.w);
         }
-        *(f32x4*)(a.comp + 4 * i) = f32x4{c[0], c[1], c[2], c[3]};
+        st_stream((f32x4*)(a.comp + 4 * i), f32x4{c[0], c[1], c[2], c[3]});
     }
     if (blockIdx.x == 0) {
         const int64_t i = 4 * n4 + threadIdx.x;
@@ -613,11 +665,11 @@ __global__ __launch_bounds__(kBlock) void compensate_kernel(const CompArgs a)
             const float e = a.err[i];
             if (SLOW) {
                 float c, mo;
-                comp1(a, e, a.slow[i], c, mo);
-                a.slow[i] = mo;
+                update1(a.upd, e, a.upd.slow[i], c, mo);
+                a.upd.slow[i] = mo;
                 a.comp[i] = c;
             } else {
-                a.comp[i] = -(a.alpha * e);
+                a.comp[i] = -(a.upd.alpha * e);
             }
         }
     }

@@ -30,7 +30,7 @@
  *  - Arguments are checked on the host before anything is enqueued; a call
  *    that returns an error other than ECHO_EHIP has enqueued nothing.
  *  - Data pointers must be 16-byte aligned (ECHO_EALIGN otherwise).
- *  - Messages: n elements per rank, 0 <= n <= 2^36, n a multiple of P*group.
+ *  - Messages: n elements per rank, 0 <= n <= 2^34, n a multiple of P*group.
  *    S = n / P is the segment length.  Tiles are element ranges *inside each
  *    segment*: [tile_begin, tile_begin + tile_len), both multiples of group,
  *    tile_begin + tile_len <= S.  (0, S) means whole segments.
@@ -188,11 +188,14 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  * streams may be NULL (null stream only).  Results do not depend on tiles or
  * streams (bit for bit).
  *
- * Feedback (ef = 1): every rank's comp is added at the entry pass.  If
- * alpha == 1, beta == 0 and err[r] == NULL for every rank, the kernels write
- * -e straight into comp (classic error feedback, bit-identical to running
- * echo_compensate); otherwise err[r] receives e and echo_compensate turns it
- * into comp[r] (and slow[r]) after the call's last reduce.
+ * Feedback (ef = 1): every rank's comp is added at the entry pass.  With
+ * err[r] == NULL for every rank the update is fused into the push and reduce
+ * kernels: they write -e straight into comp (alpha = 1, beta = 0, classic
+ * error feedback) or apply the two-timescale update to comp and slow in place
+ * (beta > 0).  Both are bit-identical to writing e and running
+ * echo_compensate, which is what happens when err[r] are given: err[r]
+ * receives e, and echo_compensate turns it into comp[r] (and slow[r]) after
+ * the call's last reduce.
  *
  * The workspace (device, caller-allocated, >= echo_allreduce_sim_workspace_bytes)
  * holds every rank's push codes/params and the sum codes/params.
@@ -210,7 +213,7 @@ typedef struct echo_sim_args {
     const uint16_t* x[ECHO_MAX_P]; /* (device) bf16 bits [n] per rank */
     float* comp[ECHO_MAX_P];       /* (device) fp32 [n] per rank (ef = 1) */
     float* slow[ECHO_MAX_P];       /* (device) fp32 [n] per rank (beta > 0) */
-    float* err[ECHO_MAX_P];        /* (device) fp32 [n] per rank, or NULL (fused classic) */
+    float* err[ECHO_MAX_P];        /* (device) fp32 [n] per rank, or NULL (update fused) */
     void* out[ECHO_MAX_P];         /* (device) [n] fp32 or bf16 bits per rank */
     void* workspace;               /* (device) */
     size_t workspace_bytes;

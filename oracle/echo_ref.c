@@ -438,10 +438,10 @@ int echo_ref_compensate(const float* err, float* comp_next, float* slow, int64_t
 /* One whole all-reduce call over P ranks held in host memory: push for     */
 /* every rank, reduce for every owner, decode for every rank, then the      */
 /* compensator.  ef = 0: no compensation (comp/err/slow ignored).            */
-/* ef = 1: u = x + comp; if err is NULL the update must be classic           */
-/* (alpha = 1, beta = 0) and -e is written straight into comp (identical to  */
-/* computing e and then c' = -(1*e)); otherwise e goes to err and            */
-/* echo_ref_compensate turns it into comp (and slow).                        */
+/* ef = 1: u = x + comp; e goes to err (temporary arrays when err is NULL)   */
+/* and echo_ref_compensate turns it into comp (and slow).  For the classic   */
+/* update (alpha = 1, beta = 0) with err NULL, -e is written straight into  */
+/* comp, identical to computing e and then c' = -(1*e).                     */
 /* Instrumentation ([EchoCard] abstract and Fig. 2: at most two              */
 /* quantizations per element per call), filled from counters that the push  */
 /* and reduce loops above increment as they run:                             */
@@ -461,8 +461,16 @@ int echo_ref_allreduce(int P, int64_t n, int bits, int g, int ef, float alpha, f
     if (out_dtype != REF_OUT_F32 && out_dtype != REF_OUT_BF16) return REF_EUNSUP;
     int64_t S = n / P;
     int fused = ef && !err;
-    if (ef && fused && !(alpha == 1.0f && beta == 0.0f)) return REF_EINVAL;
     if (ef && !comp) return REF_EINVAL;
+    /* a two-timescale update requested without error buffers is defined as
+     * the unfused update: errors go to temporary arrays, then the compensator */
+    float** tmp_err = NULL;
+    if (ef && fused && !(alpha == 1.0f && beta == 0.0f)) {
+        tmp_err = (float**)calloc((size_t)P, sizeof(float*));
+        for (int r = 0; r < P; ++r) tmp_err[r] = (float*)calloc((size_t)n + 1, sizeof(float));
+        err = tmp_err;
+        fused = 0;
+    }
     int counting = qdepth || qwork;
     size_t cbytes = bits == 4 ? (size_t)(n / 2) : (size_t)n;
     size_t pwords = 2 * (size_t)(n / g);
@@ -514,5 +522,9 @@ int echo_ref_allreduce(int P, int64_t n, int bits, int g, int ef, float alpha, f
     }
     for (int r = 0; r < P; ++r) { free(pc[r]); free(pp[r]); free(pushcnt[r]); }
     free(pc); free(pp); free(pushcnt); free(sc); free(sp); free(sumcnt);
+    if (tmp_err) {
+        for (int r = 0; r < P; ++r) free(tmp_err[r]);
+        free(tmp_err);
+    }
     return rc;
 }

@@ -22,15 +22,19 @@ def echo():
     return e
 
 
+MODES = {"off": (1.0, 0.0), "classic": (1.0, 0.0), "classic_unfused": (1.0, 0.0), "two": (0.5, 0.25),
+         "two_fused": (0.5, 0.25)}
+
+
 def run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams):
     """Run len(xs_list) consecutive calls; returns per-call outs and the final state."""
-    alpha, beta = {"off": (1.0, 0.0), "classic": (1.0, 0.0), "classic_unfused": (1.0, 0.0),
-                   "two": (0.5, 0.25)}[ef_mode]
+    alpha, beta = MODES[ef_mode]
     ef = ef_mode != "off"
     comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if ef else None
     errs = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] \
         if ef_mode in ("classic_unfused", "two") else None
-    slows = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if ef_mode == "two" else None
+    slows = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] \
+        if ef_mode in ("two", "two_fused") else None
     odtype = torch.float32 if odt == oracle.OUT_F32 else torch.int16
     ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
     streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
@@ -50,12 +54,13 @@ def run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams):
 
 
 def run_oracle_calls(xs_list, P, n, bits, ef_mode, odt):
-    alpha, beta = {"off": (1.0, 0.0), "classic": (1.0, 0.0), "classic_unfused": (1.0, 0.0),
-                   "two": (0.5, 0.25)}[ef_mode]
+    alpha, beta = MODES[ef_mode]
     ef = ef_mode != "off"
     comps = [np.zeros(n, np.float32) for _ in range(P)] if ef else None
-    errs = [np.zeros(n, np.float32) for _ in range(P)] if ef_mode in ("classic_unfused", "two") else None
-    slows = [np.zeros(n, np.float32) for _ in range(P)] if ef_mode == "two" else None
+    # the oracle always runs the unfused update (explicit error arrays)
+    errs = [np.zeros(n, np.float32) for _ in range(P)] if ef_mode in ("classic_unfused", "two", "two_fused") \
+        else None
+    slows = [np.zeros(n, np.float32) for _ in range(P)] if ef_mode in ("two", "two_fused") else None
     results = []
     for xs in xs_list:
         outs, _, _ = oracle.allreduce(xs, bits=bits, ef=ef, alpha=alpha, beta=beta, comps=comps, slows=slows,
@@ -78,6 +83,11 @@ CASES = [
     (8, 4, "classic", oracle.OUT_BF16, 4, 4),
     (8, 8, "two", oracle.OUT_BF16, 2, 4),
     (5, 4, "classic", oracle.OUT_F32, 3, 4),
+    (4, 4, "two_fused", oracle.OUT_F32, 1, 1),
+    (4, 4, "two_fused", oracle.OUT_BF16, 6, 4),
+    (8, 8, "two_fused", oracle.OUT_F32, 3, 2),
+    (2, 4, "two_fused", oracle.OUT_F32, 2, 3),
+    (1, 8, "two_fused", oracle.OUT_F32, 1, 1),
 ]
 
 
@@ -96,7 +106,7 @@ def test_sim_matches_oracle_over_calls(echo, P, bits, ef_mode, odt, tiles, nstre
             assert_bits_equal(got[c][r], want[c][r], f"call {c} rank {r} out bits")
             assert_bits_equal(got[c][r], got[c][0], f"call {c}: rank {r} differs from rank 0")
     for key in ("comps", "slows", "errs"):
-        if wstate[key] is not None:
+        if wstate[key] is not None and gstate[key] is not None:
             for r in range(P):
                 assert_f32_parity(gstate[key][r], wstate[key][r], f"{key}[{r}]")
                 assert_bits_equal(gstate[key][r], wstate[key][r], f"{key}[{r}] bits")
