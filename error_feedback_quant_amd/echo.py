@@ -19,6 +19,12 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "echo.h")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+# torch brings its own HIP runtime (libamdhip64, SONAME libamdhip64.so.7) and
+# owns the device memory and streams passed to libecho, so it must be loaded
+# first: libecho.so then binds to that same runtime instead of pulling a
+# second copy into the process.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, EINVAL, EALIGN, EUNSUP, ESHAPE, EHIP = 0, -1, -2, -3, -4, -5
