@@ -24,10 +24,20 @@ namespace {
 thread_local int t_last_hip_error = 0;
 
 constexpr int64_t kMaxN = int64_t(1) << 34;
-#ifndef ECHO_U
-#define ECHO_U 2
+// passes of 16 groups per block (each DPP row handles this many groups),
+// per kernel; chosen by measurement at the 1 GiB workload
+#ifndef ECHO_U_PUSH
+#define ECHO_U_PUSH 2
 #endif
-constexpr int kU = ECHO_U;  // passes of 16 groups per block (groups per DPP row)
+#ifndef ECHO_U_RED
+#define ECHO_U_RED 2
+#endif
+#ifndef ECHO_U_GATH
+#define ECHO_U_GATH 2
+#endif
+constexpr int kUPush = ECHO_U_PUSH;
+constexpr int kURed = ECHO_U_RED;
+constexpr int kUGath = ECHO_U_GATH;
 
 int hip_fail(hipError_t e)
 {
@@ -70,7 +80,10 @@ int check_alpha_beta(float alpha, float beta)
 // the slow memory is given exactly when it is released (beta > 0)
 int check_slow(float beta, bool has_slow) { return has_slow == (beta > 0.0f) ? ECHO_OK : ECHO_EINVAL; }
 
-unsigned blocks_for(uint32_t tile_groups) { return (tile_groups + echo::kRowsPerBlock * kU - 1) / (echo::kRowsPerBlock * kU); }
+unsigned blocks_for(uint32_t tile_groups, int u)
+{
+    return (tile_groups + echo::kRowsPerBlock * u - 1) / (echo::kRowsPerBlock * u);
+}
 
 // ---------------------------------------------------------------- launchers --
 // Each assumes validated arguments and tile_len > 0.
@@ -98,14 +111,14 @@ int launch_push(const uint16_t* x, const float* comp, int64_t n, int P, int rank
     a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
     a.rank = rank; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
     if (upd) a.upd = *upd;
-    dim3 grid(blocks_for(a.tile_groups), (unsigned)(P - 1));
+    dim3 grid(blocks_for(a.tile_groups, kUPush), (unsigned)(P - 1));
     dim3 block(echo::kBlock);
     if (bits == 4) {
-        if (upd) hipLaunchKernelGGL((echo::push_kernel<4, kU, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((echo::push_kernel<4, kU, false>), grid, block, 0, st, a);
+        if (upd) hipLaunchKernelGGL((echo::push_kernel<4, kUPush, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((echo::push_kernel<4, kUPush, false>), grid, block, 0, st, a);
     } else {
-        if (upd) hipLaunchKernelGGL((echo::push_kernel<8, kU, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((echo::push_kernel<8, kU, false>), grid, block, 0, st, a);
+        if (upd) hipLaunchKernelGGL((echo::push_kernel<8, kUPush, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((echo::push_kernel<8, kUPush, false>), grid, block, 0, st, a);
     }
     return check_launch();
 }
@@ -115,14 +128,14 @@ void launch_reduce_p(const echo::ReduceArgs& a, int P, dim3 grid, hipStream_t st
 {
     dim3 block(echo::kBlock);
     switch (P) {
-    case 1: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 1, kU, UPD>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 2, kU, UPD>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 3, kU, UPD>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 4, kU, UPD>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 5, kU, UPD>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 6, kU, UPD>), grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 7, kU, UPD>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 8, kU, UPD>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 1, kURed, UPD>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 2, kURed, UPD>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 3, kURed, UPD>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 4, kURed, UPD>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 5, kURed, UPD>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 6, kURed, UPD>), grid, block, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 7, kURed, UPD>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 8, kURed, UPD>), grid, block, 0, st, a); break;
     }
 }
 
@@ -142,7 +155,7 @@ int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc
     a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
     a.owner = owner; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
     if (upd) a.upd = *upd;
-    dim3 grid(blocks_for(a.tile_groups), 1);
+    dim3 grid(blocks_for(a.tile_groups, kURed), 1);
     if (bits == 4) {
         if (upd) launch_reduce_p<4, true>(a, P, grid, st);
         else launch_reduce_p<4, false>(a, P, grid, st);
@@ -159,14 +172,14 @@ int launch_gather(const uint8_t* sc, const echo_qparam* sp, int64_t n, int64_t t
     echo::GatherArgs a;
     a.sc = sc; a.sp = (const uint32_t*)sp; a.out = out;
     a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
-    dim3 grid(blocks_for(a.tile_groups), (unsigned)P);
+    dim3 grid(blocks_for(a.tile_groups, kUGath), (unsigned)P);
     const bool bf = out_dtype == ECHO_OUT_BF16;
     if (bits == 4) {
-        if (bf) hipLaunchKernelGGL((echo::gather_kernel<4, true, kU>), grid, dim3(echo::kBlock), 0, st, a);
-        else hipLaunchKernelGGL((echo::gather_kernel<4, false, kU>), grid, dim3(echo::kBlock), 0, st, a);
+        if (bf) hipLaunchKernelGGL((echo::gather_kernel<4, true, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
+        else hipLaunchKernelGGL((echo::gather_kernel<4, false, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
     } else {
-        if (bf) hipLaunchKernelGGL((echo::gather_kernel<8, true, kU>), grid, dim3(echo::kBlock), 0, st, a);
-        else hipLaunchKernelGGL((echo::gather_kernel<8, false, kU>), grid, dim3(echo::kBlock), 0, st, a);
+        if (bf) hipLaunchKernelGGL((echo::gather_kernel<8, true, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
+        else hipLaunchKernelGGL((echo::gather_kernel<8, false, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
     }
     return check_launch();
 }

@@ -63,6 +63,16 @@ __device__ __forceinline__ void st_stream(T* p, const T& v)
     if constexpr (ECHO_NT) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
+// the tail's decoded output (write-only stream)
+#ifndef ECHO_NT_OUT
+#define ECHO_NT_OUT 1
+#endif
+template <typename T>
+__device__ __forceinline__ void st_out(T* p, const T& v)
+{
+    if constexpr (ECHO_NT_OUT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 // fp32 streams (compensation in, error out) go through a wave-private LDS
 // slice so that every global fp32 access is lane-contiguous (1 KB per wave
@@ -617,11 +627,11 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
             w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
             w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
             w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
-            st_stream((u32x4*)((uint16_t*)a.out + e0), w);
+            st_out((u32x4*)((uint16_t*)a.out + e0), w);
         } else {
             float* o = (float*)a.out + e0;
-            st_stream((f32x4*)o, f32x4{v[0], v[1], v[2], v[3]});
-            st_stream((f32x4*)(o + 4), f32x4{v[4], v[5], v[6], v[7]});
+            st_out((f32x4*)o, f32x4{v[0], v[1], v[2], v[3]});
+            st_out((f32x4*)(o + 4), f32x4{v[4], v[5], v[6], v[7]});
         }
     }
 }
