@@ -34,6 +34,8 @@ LIB = os.path.join(HERE, "libecho_ref.so")
 
 OK, EINVAL, EUNSUP, ESHAPE = 0, -1, -3, -4
 ERR_NEGATED = 1
+Q_NAIVE, Q_SYMMETRIC = 2, 4          # quantizer flag bits (Table 8 ablations)
+QUANTS = {"zero_aware": 0, "naive": Q_NAIVE, "symmetric": Q_SYMMETRIC}
 OUT_F32, OUT_BF16 = 0, 1
 
 CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
@@ -68,6 +70,8 @@ def lib():
         L.echo_ref_f32_to_bf16_array.argtypes = [c_void_p, c_void_p, c_int64]
         L.echo_ref_quantize_group.restype = c_int
         L.echo_ref_quantize_group.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
+        L.echo_ref_quantize_group_q.restype = c_int
+        L.echo_ref_quantize_group_q.argtypes = [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]
         L.echo_ref_dequant.restype = c_float
         L.echo_ref_dequant.argtypes = [c_int, c_uint16, c_uint16]
         L.echo_ref_quantize_ef.restype = c_int
@@ -85,7 +89,7 @@ def lib():
         L.echo_ref_allreduce.restype = c_int
         L.echo_ref_allreduce.argtypes = [c_int, c_int64, c_int, c_int, c_int, c_float, c_float,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
-                                         c_void_p, c_void_p]
+                                         c_void_p, c_void_p, c_int]
         _lib = L
     return _lib
 
@@ -141,14 +145,16 @@ def f16_bits_to_f32(h: int) -> float:
 
 # --- the quantizer -------------------------------------------------------------
 
-def quantize_group(v, bits: int):
-    """Q_b of one group.  Returns (codes uint8 [g], scale_bits, zero_bits)."""
+def quantize_group(v, bits: int, quant: str = "zero_aware"):
+    """Q_b of one group with the named quantizer ("zero_aware", "naive",
+    "symmetric").  Returns (codes uint8 [g], scale_bits, zero_bits)."""
     v = np.ascontiguousarray(v, dtype=np.float32)
     q = np.zeros(v.size, dtype=np.uint8)
     sh = ctypes.c_uint16()
     zh = ctypes.c_uint16()
-    _check("quantize_group", lib().echo_ref_quantize_group(_p(v), v.size, bits, _p(q),
-                                                           ctypes.byref(sh), ctypes.byref(zh)))
+    mode = {"zero_aware": 0, "naive": 1, "symmetric": 2}[quant]
+    _check("quantize_group", lib().echo_ref_quantize_group_q(_p(v), v.size, bits, mode, _p(q),
+                                                             ctypes.byref(sh), ctypes.byref(zh)))
     return q, int(sh.value), int(zh.value)
 
 
@@ -192,7 +198,7 @@ def compensate(err, comp_next, slow, n, alpha, beta):
 
 
 def allreduce(xs, bits=4, group=128, ef=False, alpha=1.0, beta=0.0, comps=None, slows=None,
-              errs=None, out_dtype=OUT_F32, want_counts=False):
+              errs=None, out_dtype=OUT_F32, want_counts=False, quant="zero_aware"):
     """One whole call over P ranks.  xs: list of uint16 [n] (bf16 bits).
     comps/slows/errs: lists of float32 [n] updated in place (ef=True).
     Returns (outs, qdepth, qwork)."""
@@ -209,7 +215,7 @@ def allreduce(xs, bits=4, group=128, ef=False, alpha=1.0, beta=0.0, comps=None, 
         _ptr_array(comps) if comps is not None else None,
         _ptr_array(slows) if slows is not None else None,
         _ptr_array(errs) if errs is not None else None,
-        _ptr_array(outs), out_dtype, _p(qdepth), _p(qwork))
+        _ptr_array(outs), out_dtype, _p(qdepth), _p(qwork), QUANTS[quant])
     _check("allreduce", rc)
     return outs, qdepth, qwork
 
@@ -218,7 +224,7 @@ def allreduce(xs, bits=4, group=128, ef=False, alpha=1.0, beta=0.0, comps=None, 
 # --- all-reduce outputs to the hidden state) ----------------------------------
 
 def depth_chain(partials, P, n, bits=4, group=128, ef=False, alpha=1.0, beta=0.0, fused=True,
-                comps=None, slows=None):
+                comps=None, slows=None, quant="zero_aware"):
     """Run N all-reduce calls, one per injection site, accumulating each
     call's output into a float64 hidden state h and the exact sum of all
     partials into h_exact.  `partials(site)` returns P uint16 arrays.
@@ -251,7 +257,7 @@ def depth_chain(partials, P, n, bits=4, group=128, ef=False, alpha=1.0, beta=0.0
             for c in comps:
                 csum += c.astype(np.float64)
         outs, _, _ = allreduce(xs, bits=bits, group=group, ef=ef, alpha=alpha, beta=beta,
-                               comps=comps, slows=slows if two else None, errs=errs)
+                               comps=comps, slows=slows if two else None, errs=errs, quant=quant)
         out = outs[0].astype(np.float64)
         h += out
         h_exact += xsum

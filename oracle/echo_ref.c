@@ -49,6 +49,18 @@
 #define REF_ESHAPE (-4)
 
 #define REF_ERR_NEGATED 1   /* write -e (the next call's compensation) instead of e */
+#define REF_Q_NAIVE 2       /* quantizer: naive zero point (Table 8 ablation)          */
+#define REF_Q_SYMMETRIC 4   /* quantizer: symmetric grid (Table 8 ablation)            */
+
+enum { Q_ZERO_AWARE = 0, Q_NAIVE = 1, Q_SYMMETRIC = 2 };
+
+/* quantizer selected by the flag bits; -1 when both ablations are asked for */
+static int quant_of(int flags)
+{
+    int naive = (flags & REF_Q_NAIVE) != 0, sym = (flags & REF_Q_SYMMETRIC) != 0;
+    if (naive && sym) return -1;
+    return naive ? Q_NAIVE : (sym ? Q_SYMMETRIC : Q_ZERO_AWARE);
+}
 #define REF_OUT_F32 0
 #define REF_OUT_BF16 1
 
@@ -129,13 +141,30 @@ void echo_ref_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n)
 }
 
 /* ------------------------------------------------------------------------ */
-/* O1: the zero-aware asymmetric group quantizer Q_b and its dequantizer.     */
-/* [EchoCard] Table 8 (full method: zero-aware asymmetric, g = 128); Fig. 4   */
-/* (Eqn. (8) with b = 4); [Blog] "The cancellation rule" (fp16 parameters).   */
+/* O1: the group quantizer Q_b and its dequantizer.                         */
+/* [EchoCard] Table 8 (full method: zero-aware asymmetric, g = 128; the     */
+/* ablations "naive zero-point" and "symmetric grid"); Fig. 4 (Eqn. (8)     */
+/* with b = 4); [Blog] "The cancellation rule" (half-precision parameters). */
+/* All three quantizers store a binary16 scale s and a binary16 zero point z */
+/* per group and decode alike: v_hat = (q - z) * s.                          */
 /* ------------------------------------------------------------------------ */
 
-/* Quantize one group of g values to unsigned b-bit codes (one per byte in q).
- * Steps:
+/* binary16 scale from an fp32 quotient: nearest even, a zero result becomes
+ * 2^-24 and an infinite one 65504 */
+static uint16_t scale_bits(float s32)
+{
+    uint16_t sh = echo_ref_f32_to_f16(s32);
+    if (sh == 0x0000u) sh = 0x0001u;
+    else if (sh == 0x7C00u) sh = 0x7BFFu;
+    return sh;
+}
+
+static uint8_t clamp_code(double t, int Qm)
+{
+    return (uint8_t)(t < 0.0 ? 0 : (t > (double)Qm ? Qm : (int)t));
+}
+
+/* Zero-aware asymmetric (the full method).  Steps:
  *   1. lo = min(0, min v), hi = max(0, max v): the range always holds 0.
  *   2. hi == lo means an all-zero group: scale +0, zero point 0, codes 0.
  *   3. s32 = (hi - lo) / Qm, Qm = 2^b - 1 (true fp32 division).
@@ -147,12 +176,9 @@ void echo_ref_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n)
  *   8. z is stored as binary16 (exact: an integer <= 255).
  * Pinned by: brute-force argmin over all codes on tiny groups, exact-rational
  * scale choice, the grid round-trip, zero-awareness and the element bound. */
-int echo_ref_quantize_group(const float* v, int g, int bits, uint8_t* q,
-                            uint16_t* scale_h, uint16_t* zero_h)
+static void quant_zero_aware(const float* v, int g, int Qm, uint8_t* q, uint16_t* scale_h,
+                             uint16_t* zero_h)
 {
-    if (bits != 4 && bits != 8) return REF_EUNSUP;
-    if (g < 1) return REF_EINVAL;
-    const int Qm = (1 << bits) - 1;
     float lo = 0.0f, hi = 0.0f;
     for (int i = 0; i < g; ++i) {
         if (v[i] < lo) lo = v[i];
@@ -162,31 +188,112 @@ int echo_ref_quantize_group(const float* v, int g, int bits, uint8_t* q,
         for (int i = 0; i < g; ++i) q[i] = 0;
         *scale_h = 0;
         *zero_h = 0;
-        return REF_OK;
+        return;
     }
-    float s32 = (hi - lo) / (float)Qm;
-    uint16_t sh = echo_ref_f32_to_f16(s32);
-    if (sh == 0x0000u) sh = 0x0001u;        /* underflow -> 2^-24 */
-    else if (sh == 0x7C00u) sh = 0x7BFFu;   /* overflow  -> 65504 */
+    uint16_t sh = scale_bits((hi - lo) / (float)Qm);
     float s = echo_ref_f16_to_f32(sh);
     float inv = 1.0f / s;
-    double zr = (double)rintf(-lo * inv);
-    int z = zr < 0.0 ? 0 : (zr > (double)Qm ? Qm : (int)zr);
-    for (int i = 0; i < g; ++i) {
-        double t = (double)rintf(v[i] * inv) + (double)z;
-        q[i] = (uint8_t)(t < 0.0 ? 0 : (t > (double)Qm ? Qm : (int)t));
-    }
+    int z = clamp_code((double)rintf(-lo * inv), Qm);
+    for (int i = 0; i < g; ++i) q[i] = clamp_code((double)rintf(v[i] * inv) + (double)z, Qm);
     *scale_h = sh;
     *zero_h = echo_ref_f32_to_f16((float)z);
-    return REF_OK;
 }
 
-/* Dequantizer: v_hat = (q - z) * s.  Exact in fp32: |q - z| <= 255 needs 8
- * bits and s has an 11-bit significand, so the product fits in 24 bits. */
+/* Naive zero point (Table 8 ablation; reading: the textbook min/max affine
+ * quantizer with a real-valued zero point, so 0 is generally not a grid
+ * point).  Steps:
+ *   1. lo = min v, hi = max v (the range is not widened to hold 0).
+ *   2. hi == lo: scale +0, zero point 0, codes 0 (the group decodes to 0).
+ *   3. s = binary16((hi - lo) / Qm) with the clamps of the full method.
+ *   4. inv = 1 / s; z = binary16(-lo * inv), an overflow clamped to +-65504.
+ *   5. q_i = clamp(rint(v_i * inv + z), 0, Qm): the zero point is added
+ *      before rounding (two fp32 roundings, then rint).
+ * Pinned by: brute force over codes and exact-rational choice of s and z on
+ * tiny groups, the grid round-trip, and the existence of groups where 0 does
+ * not decode to 0. */
+static void quant_naive(const float* v, int g, int Qm, uint8_t* q, uint16_t* scale_h, uint16_t* zero_h)
+{
+    float lo = v[0], hi = v[0];
+    for (int i = 1; i < g; ++i) {
+        if (v[i] < lo) lo = v[i];
+        if (v[i] > hi) hi = v[i];
+    }
+    if (hi == lo) {
+        for (int i = 0; i < g; ++i) q[i] = 0;
+        *scale_h = 0;
+        *zero_h = 0;
+        return;
+    }
+    uint16_t sh = scale_bits((hi - lo) / (float)Qm);
+    float s = echo_ref_f16_to_f32(sh);
+    float inv = 1.0f / s;
+    uint16_t zh = echo_ref_f32_to_f16(-lo * inv);
+    if ((zh & 0x7FFFu) == 0x7C00u) zh = (uint16_t)((zh & 0x8000u) | 0x7BFFu);
+    float zf = echo_ref_f16_to_f32(zh);
+    for (int i = 0; i < g; ++i) q[i] = clamp_code((double)rintf(v[i] * inv + zf), Qm);
+    *scale_h = sh;
+    *zero_h = zh;
+}
+
+/* Symmetric grid (Table 8 ablation; reading: a grid symmetric about 0 with
+ * the zero point fixed at the middle code).  Steps, with Qh = 2^(b-1) - 1 and
+ * mid = 2^(b-1):
+ *   1. a = max |v|.
+ *   2. a == 0: scale +0, zero point mid, codes mid (decode to 0).
+ *   3. s = binary16(a / Qh) with the clamps of the full method; inv = 1 / s.
+ *   4. q_i = clamp(rint(v_i * inv) + mid, 0, Qm), so codes use mid +- Qh.
+ * Pinned by: brute force over codes and exact-rational scale choice,
+ * zero-awareness and the grid round-trip. */
+static void quant_symmetric(const float* v, int g, int bits, uint8_t* q, uint16_t* scale_h,
+                            uint16_t* zero_h)
+{
+    const int Qm = (1 << bits) - 1, Qh = (1 << (bits - 1)) - 1, mid = 1 << (bits - 1);
+    float a = 0.0f;
+    for (int i = 0; i < g; ++i)
+        if (fabsf(v[i]) > a) a = fabsf(v[i]);
+    *zero_h = echo_ref_f32_to_f16((float)mid);
+    if (a == 0.0f) {
+        for (int i = 0; i < g; ++i) q[i] = (uint8_t)mid;
+        *scale_h = 0;
+        return;
+    }
+    uint16_t sh = scale_bits(a / (float)Qh);
+    float s = echo_ref_f16_to_f32(sh);
+    float inv = 1.0f / s;
+    for (int i = 0; i < g; ++i) q[i] = clamp_code((double)rintf(v[i] * inv) + (double)mid, Qm);
+    *scale_h = sh;
+}
+
+/* Quantize one group of g values to unsigned b-bit codes (one per byte in q)
+ * with quantizer `quant` (0 zero-aware, 1 naive zero point, 2 symmetric). */
+int echo_ref_quantize_group_q(const float* v, int g, int bits, int quant, uint8_t* q,
+                              uint16_t* scale_h, uint16_t* zero_h)
+{
+    if (bits != 4 && bits != 8) return REF_EUNSUP;
+    if (g < 1) return REF_EINVAL;
+    const int Qm = (1 << bits) - 1;
+    switch (quant) {
+    case Q_ZERO_AWARE: quant_zero_aware(v, g, Qm, q, scale_h, zero_h); return REF_OK;
+    case Q_NAIVE: quant_naive(v, g, Qm, q, scale_h, zero_h); return REF_OK;
+    case Q_SYMMETRIC: quant_symmetric(v, g, bits, q, scale_h, zero_h); return REF_OK;
+    default: return REF_EINVAL;
+    }
+}
+
+/* The full method's quantizer (zero-aware asymmetric). */
+int echo_ref_quantize_group(const float* v, int g, int bits, uint8_t* q,
+                            uint16_t* scale_h, uint16_t* zero_h)
+{
+    return echo_ref_quantize_group_q(v, g, bits, Q_ZERO_AWARE, q, scale_h, zero_h);
+}
+
+/* Dequantizer: v_hat = (q - z) * s in fp32.  q - z is exact (q <= 255 and z
+ * a binary16 value); with an integer z (zero-aware, symmetric) the product
+ * is exact too: |q - z| <= 255 needs 8 bits and s has an 11-bit significand. */
 float echo_ref_dequant(int q, uint16_t scale_h, uint16_t zero_h)
 {
-    int z = (int)echo_ref_f16_to_f32(zero_h);
-    return (float)(q - z) * echo_ref_f16_to_f32(scale_h);
+    float d = (float)q - echo_ref_f16_to_f32(zero_h);
+    return d * echo_ref_f16_to_f32(scale_h);
 }
 
 /* Packed code stream: b = 4 -> element i in byte i/2, low nibble when i is
@@ -212,11 +319,11 @@ static void code_put(uint8_t* codes, int64_t i, int bits, int q)
 /* Quantize the g values u[0..g) of the group that starts at message element
  * `base` into the code stream and the parameter array; count, if not NULL,
  * is incremented for every element passed through the quantizer. */
-static void quantize_into(const float* u, int64_t base, int g, int bits,
+static void quantize_into(const float* u, int64_t base, int g, int bits, int quant,
                           uint8_t* codes, uint16_t* params, uint8_t* qscratch, int* count)
 {
     uint16_t sh, zh;
-    echo_ref_quantize_group(u, g, bits, qscratch, &sh, &zh);
+    echo_ref_quantize_group_q(u, g, bits, quant, qscratch, &sh, &zh);
     for (int i = 0; i < g; ++i) code_put(codes, base + i, bits, qscratch[i]);
     params[2 * (base / g)] = sh;
     params[2 * (base / g) + 1] = zh;
@@ -260,6 +367,8 @@ static int push_impl(const uint16_t* x, const float* comp, int64_t n, int P, int
     if (rc) return rc;
     if (rank < 0 || rank >= P) return REF_EINVAL;
     if ((!x || !codes || !params) && n > 0) return REF_EINVAL;
+    const int quant = quant_of(flags);
+    if (quant < 0) return REF_EINVAL;
     int64_t S = n / P;
     float* u = (float*)malloc(sizeof(float) * (size_t)g);
     uint8_t* qs = (uint8_t*)malloc((size_t)g);
@@ -271,7 +380,7 @@ static int push_impl(const uint16_t* x, const float* comp, int64_t n, int P, int
                 float xv = echo_ref_bf16_to_f32(x[base + i]);
                 u[i] = comp ? xv + comp[base + i] : xv;
             }
-            quantize_into(u, base, g, bits, codes, params, qs, count);
+            quantize_into(u, base, g, bits, quant, codes, params, qs, count);
             if (err) {
                 uint16_t sh = params[2 * (base / g)], zh = params[2 * (base / g) + 1];
                 for (int i = 0; i < g; ++i) {
@@ -318,6 +427,8 @@ static int reduce_impl(const uint16_t* own_x, const float* own_comp,
     if ((!own_x || !sum_codes || !sum_params || !peer_codes || !peer_params) && n > 0) return REF_EINVAL;
     for (int j = 0; j < P; ++j)
         if (j != owner && n > 0 && (!peer_codes[j] || !peer_params[j])) return REF_EINVAL;
+    const int quant = quant_of(flags);
+    if (quant < 0) return REF_EINVAL;
     int64_t S = n / P;
     float* acc = (float*)malloc(sizeof(float) * (size_t)g);
     uint8_t* qs = (uint8_t*)malloc((size_t)g);
@@ -339,7 +450,7 @@ static int reduce_impl(const uint16_t* own_x, const float* own_comp,
             }
             acc[i] = sum;
         }
-        quantize_into(acc, base, g, bits, sum_codes, sum_params, qs, count);
+        quantize_into(acc, base, g, bits, quant, sum_codes, sum_params, qs, count);
         if (own_err) {
             uint16_t sh = sum_params[2 * grp], zh = sum_params[2 * grp + 1];
             for (int i = 0; i < g; ++i) {
@@ -442,6 +553,7 @@ int echo_ref_compensate(const float* err, float* comp_next, float* slow, int64_t
 /* and echo_ref_compensate turns it into comp (and slow).  For the classic   */
 /* update (alpha = 1, beta = 0) with err NULL, -e is written straight into  */
 /* comp, identical to computing e and then c' = -(1*e).                     */
+/* qflags selects the quantizer (0, REF_Q_NAIVE or REF_Q_SYMMETRIC).        */
 /* Instrumentation ([EchoCard] abstract and Fig. 2: at most two              */
 /* quantizations per element per call), filled from counters that the push  */
 /* and reduce loops above increment as they run:                             */
@@ -454,8 +566,9 @@ int echo_ref_compensate(const float* err, float* comp_next, float* slow, int64_t
 int echo_ref_allreduce(int P, int64_t n, int bits, int g, int ef, float alpha, float beta,
                        const uint16_t* const* x, float* const* comp, float* const* slow,
                        float* const* err, void* const* out, int out_dtype,
-                       int* qdepth, int64_t* qwork)
+                       int* qdepth, int64_t* qwork, int qflags)
 {
+    if (quant_of(qflags) < 0 || (qflags & ~(REF_Q_NAIVE | REF_Q_SYMMETRIC))) return REF_EINVAL;
     int rc = check_shape(n, P, 0, 0, bits, g);
     if (rc) return rc;
     if (out_dtype != REF_OUT_F32 && out_dtype != REF_OUT_BF16) return REF_EUNSUP;
@@ -486,7 +599,7 @@ int echo_ref_allreduce(int P, int64_t n, int bits, int g, int ef, float alpha, f
     uint8_t* sc = (uint8_t*)calloc(cbytes + 1, 1);
     uint16_t* sp = (uint16_t*)calloc(pwords + 1, sizeof(uint16_t));
     int* sumcnt = counting ? (int*)calloc(nc + 1, sizeof(int)) : NULL;
-    int flags = fused ? REF_ERR_NEGATED : 0;
+    int flags = (fused ? REF_ERR_NEGATED : 0) | qflags;
 
     for (int r = 0; r < P && !rc; ++r) {
         float* c = ef ? comp[r] : NULL;
