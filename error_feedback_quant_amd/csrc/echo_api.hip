@@ -30,7 +30,7 @@ constexpr int64_t kMaxN = int64_t(1) << 34;
 #define ECHO_U_PUSH 2
 #endif
 #ifndef ECHO_U_RED
-#define ECHO_U_RED 2
+#define ECHO_U_RED 1
 #endif
 #ifndef ECHO_U_GATH
 #define ECHO_U_GATH 2
@@ -59,7 +59,7 @@ int check_common(int64_t n, int P, int64_t tile_begin, int64_t tile_len, int bit
 {
     if (P < 1 || P > ECHO_MAX_P) return ECHO_EINVAL;
     if (bits != 4 && bits != 8) return ECHO_EUNSUP;
-    if (group != echo::kGroup) return ECHO_EUNSUP;
+    if (group != 128 && group != 256) return ECHO_EUNSUP;
     if (n < 0 || n > kMaxN || n % ((int64_t)P * group) != 0) return ECHO_ESHAPE;
     const int64_t S = n / P;
     if (tile_begin < 0 || tile_len < 0 || tile_begin % group || tile_len % group ||
@@ -80,10 +80,54 @@ int check_alpha_beta(float alpha, float beta)
 // the slow memory is given exactly when it is released (beta > 0)
 int check_slow(float beta, bool has_slow) { return has_slow == (beta > 0.0f) ? ECHO_OK : ECHO_EINVAL; }
 
-unsigned blocks_for(uint32_t tile_groups, int u)
+unsigned blocks_for(uint32_t tile_rows, int u)
 {
-    return (tile_groups + echo::kRowsPerBlock * u - 1) / (echo::kRowsPerBlock * u);
+    return (tile_rows + echo::kRowsPerBlock * u - 1) / (echo::kRowsPerBlock * u);
 }
+
+// quantizer selected by the flag bits (-1: both ablations asked for)
+int quant_of(int flags)
+{
+    const bool naive = flags & ECHO_QUANT_NAIVE, sym = flags & ECHO_QUANT_SYMMETRIC;
+    if (naive && sym) return -1;
+    return naive ? echo::kNaive : (sym ? echo::kSymmetric : echo::kZeroAware);
+}
+
+constexpr int kKnownFlags = ECHO_ERR_NEGATED | ECHO_QUANT_NAIVE | ECHO_QUANT_SYMMETRIC;
+
+// Runtime (bits, update, quantizer, group) -> kernel template instance.
+template <template <int, bool, int, int> class L, typename A>
+void dispatch(int bits, bool upd, int quant, int group, const A& a, dim3 grid, hipStream_t st)
+{
+#define ECHO_D3(B, UP, Q)                                             \
+    if (group == 128) L<B, UP, Q, 128>::go(a, grid, st);              \
+    else L<B, UP, Q, 256>::go(a, grid, st);
+#define ECHO_D2(B, UP)                                                \
+    if (quant == echo::kNaive) { ECHO_D3(B, UP, echo::kNaive) }       \
+    else if (quant == echo::kSymmetric) { ECHO_D3(B, UP, echo::kSymmetric) } \
+    else { ECHO_D3(B, UP, echo::kZeroAware) }
+#define ECHO_D1(B)                                                    \
+    if (upd) { ECHO_D2(B, true) } else { ECHO_D2(B, false) }
+    if (bits == 4) { ECHO_D1(4) } else { ECHO_D1(8) }
+#undef ECHO_D1
+#undef ECHO_D2
+#undef ECHO_D3
+}
+
+template <int B, bool UP, int Q, int G>
+struct PushL {
+    static void go(const echo::PushArgs& a, dim3 grid, hipStream_t st)
+    {
+        hipLaunchKernelGGL((echo::push_kernel<B, kUPush, UP, Q, G>), grid, dim3(echo::kBlock), 0, st, a);
+    }
+};
+template <int B, bool UP, int Q, int G>
+struct ReduceL {
+    static void go(const echo::ReduceArgs& a, dim3 grid, hipStream_t st)
+    {
+        hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G>), grid, dim3(echo::kBlock), 0, st, a);
+    }
+};
 
 // ---------------------------------------------------------------- launchers --
 // Each assumes validated arguments and tile_len > 0.
@@ -101,47 +145,24 @@ echo::UpdArgs make_upd(float* slow, float alpha, float beta)
 
 // upd != nullptr: fused two-timescale update (comp and upd->slow in place, err unused)
 int launch_push(const uint16_t* x, const float* comp, int64_t n, int P, int rank, int64_t tb,
-                int64_t tl, int bits, uint8_t* codes, echo_qparam* params, float* err, int flags,
-                const echo::UpdArgs* upd, hipStream_t st)
+                int64_t tl, int bits, int group, uint8_t* codes, echo_qparam* params, float* err,
+                int flags, const echo::UpdArgs* upd, hipStream_t st)
 {
     if (P == 1) return ECHO_OK;   // a single rank owns everything: nothing to push
     echo::PushArgs a;
     std::memset(&a, 0, sizeof(a));
     a.x = x; a.comp = comp; a.codes = codes; a.params = (uint32_t*)params; a.err = err;
-    a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
+    a.S = n / P; a.tile_begin = tb; a.tile_rows = (uint32_t)(tl / echo::kRow);
     a.rank = rank; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
     if (upd) a.upd = *upd;
-    dim3 grid(blocks_for(a.tile_groups, kUPush), (unsigned)(P - 1));
-    dim3 block(echo::kBlock);
-    if (bits == 4) {
-        if (upd) hipLaunchKernelGGL((echo::push_kernel<4, kUPush, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((echo::push_kernel<4, kUPush, false>), grid, block, 0, st, a);
-    } else {
-        if (upd) hipLaunchKernelGGL((echo::push_kernel<8, kUPush, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((echo::push_kernel<8, kUPush, false>), grid, block, 0, st, a);
-    }
+    dim3 grid(blocks_for(a.tile_rows, kUPush), (unsigned)(P - 1));
+    dispatch<PushL>(bits, upd != nullptr, quant_of(flags), group, a, grid, st);
     return check_launch();
-}
-
-template <int BITS, bool UPD>
-void launch_reduce_p(const echo::ReduceArgs& a, int P, dim3 grid, hipStream_t st)
-{
-    dim3 block(echo::kBlock);
-    switch (P) {
-    case 1: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 1, kURed, UPD>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 2, kURed, UPD>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 3, kURed, UPD>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 4, kURed, UPD>), grid, block, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 5, kURed, UPD>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 6, kURed, UPD>), grid, block, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 7, kURed, UPD>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((echo::reduce_kernel<BITS, 8, kURed, UPD>), grid, block, 0, st, a); break;
-    }
 }
 
 int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc,
                   const echo_qparam* const* pp, int P, int owner, int64_t n, int64_t tb, int64_t tl,
-                  int bits, uint8_t* sc, echo_qparam* sp, float* err, int flags,
+                  int bits, int group, uint8_t* sc, echo_qparam* sp, float* err, int flags,
                   const echo::UpdArgs* upd, hipStream_t st)
 {
     echo::ReduceArgs a;
@@ -152,34 +173,34 @@ int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc
         a.pp[j] = j == owner ? nullptr : (const uint32_t*)pp[j];
     }
     a.sc = sc; a.sp = (uint32_t*)sp; a.err = err;
-    a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
-    a.owner = owner; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    a.S = n / P; a.tile_begin = tb; a.tile_rows = (uint32_t)(tl / echo::kRow);
+    a.P = P; a.owner = owner; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
     if (upd) a.upd = *upd;
-    dim3 grid(blocks_for(a.tile_groups, kURed), 1);
-    if (bits == 4) {
-        if (upd) launch_reduce_p<4, true>(a, P, grid, st);
-        else launch_reduce_p<4, false>(a, P, grid, st);
-    } else {
-        if (upd) launch_reduce_p<8, true>(a, P, grid, st);
-        else launch_reduce_p<8, false>(a, P, grid, st);
-    }
+    dim3 grid(blocks_for(a.tile_rows, kURed), 1);
+    dispatch<ReduceL>(bits, upd != nullptr, quant_of(flags), group, a, grid, st);
     return check_launch();
 }
 
+template <int B, bool BF, int G>
+void gather_go(const echo::GatherArgs& a, dim3 grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((echo::gather_kernel<B, BF, kUGath, G>), grid, dim3(echo::kBlock), 0, st, a);
+}
+
 int launch_gather(const uint8_t* sc, const echo_qparam* sp, int64_t n, int64_t tb, int64_t tl, int P,
-                  int bits, void* out, int out_dtype, hipStream_t st)
+                  int bits, int group, void* out, int out_dtype, hipStream_t st)
 {
     echo::GatherArgs a;
     a.sc = sc; a.sp = (const uint32_t*)sp; a.out = out;
-    a.S = n / P; a.tile_begin = tb; a.tile_groups = (uint32_t)(tl / echo::kGroup);
-    dim3 grid(blocks_for(a.tile_groups, kUGath), (unsigned)P);
+    a.S = n / P; a.tile_begin = tb; a.tile_rows = (uint32_t)(tl / echo::kRow);
+    dim3 grid(blocks_for(a.tile_rows, kUGath), (unsigned)P);
     const bool bf = out_dtype == ECHO_OUT_BF16;
     if (bits == 4) {
-        if (bf) hipLaunchKernelGGL((echo::gather_kernel<4, true, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
-        else hipLaunchKernelGGL((echo::gather_kernel<4, false, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
+        if (group == 128) { if (bf) gather_go<4, true, 128>(a, grid, st); else gather_go<4, false, 128>(a, grid, st); }
+        else { if (bf) gather_go<4, true, 256>(a, grid, st); else gather_go<4, false, 256>(a, grid, st); }
     } else {
-        if (bf) hipLaunchKernelGGL((echo::gather_kernel<8, true, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
-        else hipLaunchKernelGGL((echo::gather_kernel<8, false, kUGath>), grid, dim3(echo::kBlock), 0, st, a);
+        if (group == 128) { if (bf) gather_go<8, true, 128>(a, grid, st); else gather_go<8, false, 128>(a, grid, st); }
+        else { if (bf) gather_go<8, true, 256>(a, grid, st); else gather_go<8, false, 256>(a, grid, st); }
     }
     return check_launch();
 }
@@ -278,14 +299,14 @@ int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P
     int rc = check_common(n, P, tile_begin, tile_len, bits, group);
     if (rc) return rc;
     if (rank < 0 || rank >= P) return ECHO_EINVAL;
-    if (flags & ~ECHO_ERR_NEGATED) return ECHO_EINVAL;
+    if ((flags & ~kKnownFlags) || quant_of(flags) < 0) return ECHO_EINVAL;
     if (n == 0 || tile_len == 0 || P == 1) return ECHO_OK;
     if (!x_bf16 || !codes || !params) return ECHO_EINVAL;
     if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(params) ||
         (comp && !aligned16(comp)) || (err && !aligned16(err)))
         return ECHO_EALIGN;
-    return launch_push(x_bf16, comp, n, P, rank, tile_begin, tile_len, bits, codes, params, err, flags,
-                       nullptr, (hipStream_t)stream);
+    return launch_push(x_bf16, comp, n, P, rank, tile_begin, tile_len, bits, group, codes, params, err,
+                       flags, nullptr, (hipStream_t)stream);
 }
 
 int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
@@ -297,7 +318,7 @@ int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
     int rc = check_common(n, P, tile_begin, tile_len, bits, group);
     if (rc) return rc;
     if (owner < 0 || owner >= P) return ECHO_EINVAL;
-    if (flags & ~ECHO_ERR_NEGATED) return ECHO_EINVAL;
+    if ((flags & ~kKnownFlags) || quant_of(flags) < 0) return ECHO_EINVAL;
     if (n == 0 || tile_len == 0) return ECHO_OK;
     if (!own_x_bf16 || !sum_codes || !sum_params) return ECHO_EINVAL;
     if (P > 1 && (!peer_codes || !peer_params)) return ECHO_EINVAL;
@@ -310,7 +331,7 @@ int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
         (own_comp && !aligned16(own_comp)) || (own_err && !aligned16(own_err)))
         return ECHO_EALIGN;
     return launch_reduce(own_x_bf16, own_comp, peer_codes, peer_params, P, owner, n, tile_begin, tile_len,
-                         bits, sum_codes, sum_params, own_err, flags, nullptr, (hipStream_t)stream);
+                         bits, group, sum_codes, sum_params, own_err, flags, nullptr, (hipStream_t)stream);
 }
 
 int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params, int64_t n,
@@ -323,7 +344,7 @@ int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params,
     if (n == 0 || tile_len == 0) return ECHO_OK;
     if (!sum_codes || !sum_params || !out) return ECHO_EINVAL;
     if (!aligned16(sum_codes) || !aligned16(sum_params) || !aligned16(out)) return ECHO_EALIGN;
-    return launch_gather(sum_codes, sum_params, n, tile_begin, tile_len, P, bits, out, out_dtype,
+    return launch_gather(sum_codes, sum_params, n, tile_begin, tile_len, P, bits, group, out, out_dtype,
                          (hipStream_t)stream);
 }
 
@@ -355,6 +376,7 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
     if (a->out_dtype != ECHO_OUT_F32 && a->out_dtype != ECHO_OUT_BF16) return ECHO_EUNSUP;
     if (a->tiles < 1) return ECHO_EINVAL;
     if (a->ef != 0 && a->ef != 1) return ECHO_EINVAL;
+    if ((a->quant & ~(ECHO_QUANT_NAIVE | ECHO_QUANT_SYMMETRIC)) || quant_of(a->quant) < 0) return ECHO_EINVAL;
     if (streams && nstreams < 1) return ECHO_EINVAL;
     const int64_t n = a->n;
     if (n == 0) return ECHO_OK;
@@ -441,7 +463,7 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
     // fused (comp and slow updated in the kernels), or unfused (e into err,
     // then echo_compensate after the last reduce)
     const bool two_fused = a->ef && fused && a->beta > 0.0f;
-    const int flags = (fused && !two_fused) ? ECHO_ERR_NEGATED : 0;
+    const int flags = ((fused && !two_fused) ? ECHO_ERR_NEGATED : 0) | a->quant;
     echo::UpdArgs upd_r[ECHO_MAX_P];
     for (int r = 0; r < P; ++r) upd_r[r] = make_upd(a->slow[r], a->alpha, a->beta);
     for (int64_t t = 0; t < T; ++t) {
@@ -451,8 +473,9 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         for (int r = 0; r < P; ++r) {
             const float* c = a->ef ? a->comp[r] : nullptr;
             float* e = a->ef ? (fused ? a->comp[r] : a->err[r]) : nullptr;
-            rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, (uint8_t*)pc[r], (echo_qparam*)pp[r],
-                             two_fused ? nullptr : e, flags, two_fused ? &upd_r[r] : nullptr, s_push);
+            rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, a->group, (uint8_t*)pc[r],
+                             (echo_qparam*)pp[r], two_fused ? nullptr : e, flags,
+                             two_fused ? &upd_r[r] : nullptr, s_push);
             if (rc) return rc;
         }
         if (multi) {
@@ -463,8 +486,8 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         for (int o = 0; o < P; ++o) {
             const float* c = a->ef ? a->comp[o] : nullptr;
             float* e = a->ef ? (fused ? a->comp[o] : a->err[o]) : nullptr;
-            rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, sc, sp, two_fused ? nullptr : e,
-                               flags, two_fused ? &upd_r[o] : nullptr, s_red);
+            rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, a->group, sc, sp,
+                               two_fused ? nullptr : e, flags, two_fused ? &upd_r[o] : nullptr, s_red);
             if (rc) return rc;
         }
         if (multi) {
@@ -473,7 +496,7 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         }
         // gather moves no bytes here; tail: every rank decodes this tile of every segment
         for (int r = 0; r < P; ++r) {
-            rc = launch_gather(sc, sp, n, tb, tl, P, a->bits, a->out[r], a->out_dtype, s_tail);
+            rc = launch_gather(sc, sp, n, tb, tl, P, a->bits, a->group, a->out[r], a->out_dtype, s_tail);
             if (rc) return rc;
         }
     }

@@ -6,21 +6,26 @@
 // Table 8 and abstract; PhantomByte article on Echo, "The cancellation rule".
 //
 // Layout and mapping (all kernels):
-//  * A quantization group is 128 consecutive bf16 elements = 16 lanes x 8
-//    elements, i.e. one 16-lane DPP row of a 64-lane wavefront; each lane
-//    moves its 8 elements with one 16-byte load (bf16) or two (fp32).
-//  * Group min/max are reduced inside the row with four DPP steps
-//    (quad_perm xor-1, xor-2, row_ror 4, row_ror 8): no LDS, no barrier.
+//  * Addressing unit: a row of 128 consecutive elements = 16 lanes x 8
+//    elements, one 16-lane DPP row of a 64-lane wavefront; each lane moves its
+//    8 elements with one 16-byte load (bf16).  A wavefront covers 4 rows (512
+//    elements) per pass.
+//  * A quantization group is GROUP = 128 (one row) or 256 (a row pair)
+//    elements.  Group min/max are reduced with four row-local DPP steps
+//    (quad_perm xor-1, xor-2, row_ror 4, row_ror 8) and, for 256, one
+//    ds_swizzle swap-16 between the two rows: no LDS memory, no barrier.
 //    min/max are exact and order-free, so the tree cannot change results.
-//  * Every lane of a row derives the group's scale and zero point itself
-//    (same inputs, same IEEE operations), so nothing is broadcast; lane 0 of
-//    the row stores the 4-byte parameter word.
-//  * A 256-thread block handles 16 consecutive groups per pass and U passes;
+//  * Every lane of a group derives the group's scale and zero point itself
+//    (same inputs, same IEEE operations), so nothing is broadcast; the group's
+//    first lane stores the 4-byte parameter word.
+//  * A 256-thread block handles 16 consecutive rows per pass and U passes;
 //    blockIdx.y selects the segment.  All loads of a block's U passes are
 //    issued before any arithmetic to keep enough bytes in flight for HBM.
 //  * Codes are packed in registers: 8 nibbles -> one dword (4-bit) or 8
 //    bytes -> two dwords (8-bit), so a wavefront writes 256 / 512 contiguous
 //    bytes per pass.
+//  * fp32 streams (compensation, slow memory, error) move lane-contiguously
+//    through a wave-private LDS slice (see Fp32Io).
 // Arithmetic is IEEE fp32 with no contraction (built with -ffp-contract=off):
 // the division for the scale and 1/s are correctly rounded; rint rounds half
 // to even; binary16 conversion is the hardware v_cvt_f16_f32 (round to
@@ -32,11 +37,15 @@
 
 namespace echo {
 
-constexpr int kGroup = 128;
+constexpr int kRow = 128;                      // addressing unit (elements)
 constexpr int kEPL = 8;                        // elements per lane
-constexpr int kRowLanes = kGroup / kEPL;       // 16 lanes = one DPP row
+constexpr int kRowLanes = kRow / kEPL;         // 16 lanes = one DPP row
 constexpr int kBlock = 256;                    // 4 wavefronts of 64
-constexpr int kRowsPerBlock = kBlock / kRowLanes;  // 16 groups per pass
+constexpr int kRowsPerBlock = kBlock / kRowLanes;  // 16 rows per pass
+constexpr int kMaxP = 8;
+
+// quantizers (Table 8): the full method and its two ablations
+enum Quant { kZeroAware = 0, kNaive = 1, kSymmetric = 2 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -80,7 +89,7 @@ __device__ __forceinline__ void st_out(T* p, const T& v)
 #ifndef ECHO_STAGE
 #define ECHO_STAGE 1
 #endif
-constexpr int kWaveChunk = 4 * kGroup;   // 512 elements: the 4 groups (rows) of one wave
+constexpr int kWaveChunk = 4 * kRow;   // 512 elements: the 4 rows of one wave
 
 // orders this wave's LDS accesses across lanes (no block barrier needed: the
 // slice is private to the wave and the LDS executes a wave's operations in order)
@@ -97,13 +106,21 @@ __device__ __forceinline__ float dpp_f(float v)
         __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// min and max over the 16 lanes of a DPP row; every lane ends with the result
-__device__ __forceinline__ void row_minmax(float& lo, float& hi)
+// min and max over the lanes of a group (16 lanes, or 32 for GROUP = 256);
+// every lane ends with the result
+template <int GROUP>
+__device__ __forceinline__ void group_minmax(float& lo, float& hi)
 {
     lo = fminf(lo, dpp_f<0xB1>(lo));  hi = fmaxf(hi, dpp_f<0xB1>(hi));   // quad_perm [1,0,3,2]
     lo = fminf(lo, dpp_f<0x4E>(lo));  hi = fmaxf(hi, dpp_f<0x4E>(hi));   // quad_perm [2,3,0,1]
     lo = fminf(lo, dpp_f<0x124>(lo)); hi = fmaxf(hi, dpp_f<0x124>(hi));  // row_ror:4
     lo = fminf(lo, dpp_f<0x128>(lo)); hi = fmaxf(hi, dpp_f<0x128>(hi));  // row_ror:8
+    if constexpr (GROUP == 256) {
+        // rows 0<->1 and 2<->3: ds_swizzle in swap-16 mode hands every lane
+        // the value of lane ^ 16 (through the LDS crossbar, no LDS memory)
+        lo = fminf(lo, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, lo), 0x401F)));
+        hi = fmaxf(hi, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, hi), 0x401F)));
+    }
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -127,43 +144,108 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// Group parameters of the zero-aware asymmetric quantizer (Table 8's full
-// method): range widened to contain 0, binary16 scale, integer zero point.
+// Keeps an fp32 value as computed: the backend may otherwise fold an fp32
+// product straight into the binary16 conversion (one v_fma_mix rounding
+// instead of the fp32 rounding and then the binary16 one that the definition
+// asks for).  The empty register constraint emits no instruction.
+__device__ __forceinline__ float as_f32(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// binary16 scale with the clamps shared by all quantizers: a zero result
+// becomes 2^-24, an infinite one 65504
+__device__ __forceinline__ uint32_t scale_bits(float s32)
+{
+    uint32_t sb = f32_to_f16_bits(s32);
+    sb = (sb == 0u) ? 1u : sb;
+    sb = (sb == 0x7C00u) ? 0x7BFFu : sb;
+    return sb;
+}
+
+// Group parameters (one binary16 scale and one binary16 zero point per group)
 struct QParams {
     float s;        // scale as fp32 (exact binary16 value)
     float inv;      // 1/s, correctly rounded
-    float zf;       // zero point (integer-valued)
+    float zf;       // zero point as fp32 (exact binary16 value)
     uint32_t word;  // binary16 scale | binary16 zero << 16
 };
 
-template <int BITS>
+// Per-lane statistics feeding the parameters: zero-aware uses min/max with
+// 0 included, naive plain min/max, symmetric max |v| (carried in hi).
+template <int QUANT>
+__device__ __forceinline__ void lane_stats(const float* u, float& lo, float& hi)
+{
+    if constexpr (QUANT == kZeroAware) {
+        lo = 0.0f; hi = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { lo = fminf(lo, u[i]); hi = fmaxf(hi, u[i]); }
+    } else if constexpr (QUANT == kNaive) {
+        lo = u[0]; hi = u[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) { lo = fminf(lo, u[i]); hi = fmaxf(hi, u[i]); }
+    } else {
+        lo = 0.0f; hi = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hi = fmaxf(hi, fabsf(u[i]));
+    }
+}
+
+template <int BITS, int QUANT>
 __device__ __forceinline__ QParams make_params(float lo, float hi)
 {
     constexpr float kQm = (float)((1 << BITS) - 1);
-    const float s32 = (hi - lo) / kQm;
-    uint32_t sb = f32_to_f16_bits(s32);
-    sb = (sb == 0u) ? 1u : sb;             // underflow -> 2^-24
-    sb = (sb == 0x7C00u) ? 0x7BFFu : sb;   // overflow  -> 65504
-    const float s = f16_bits_to_f32(sb);
-    const float inv = 1.0f / s;
-    const float zr = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * inv), 0.0f, kQm);
-    const float zf = (float)(uint32_t)zr;  // through an integer, so a -0 becomes +0
-    const uint32_t zb = f32_to_f16_bits(zf);
-    const bool zero = (hi == lo);          // all-zero group
     QParams p;
-    p.s = zero ? 0.0f : s;
-    p.inv = zero ? 0.0f : inv;
-    p.zf = zero ? 0.0f : zf;
-    p.word = zero ? 0u : (sb | (zb << 16));
+    if constexpr (QUANT == kZeroAware) {
+        // range holds 0; integer zero point, so 0 is exactly code z
+        const uint32_t sb = scale_bits((hi - lo) / kQm);
+        const float s = f16_bits_to_f32(sb);
+        const float inv = 1.0f / s;
+        const float zr = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * inv), 0.0f, kQm);
+        const float zf = (float)(uint32_t)zr;  // through an integer, so a -0 becomes +0
+        const bool zero = (hi == lo);          // all-zero group
+        p.s = zero ? 0.0f : s;
+        p.inv = zero ? 0.0f : inv;
+        p.zf = zero ? 0.0f : zf;
+        p.word = zero ? 0u : (sb | (f32_to_f16_bits(zf) << 16));
+    } else if constexpr (QUANT == kNaive) {
+        // plain min/max range; real-valued zero point -lo/s in binary16
+        const uint32_t sb = scale_bits((hi - lo) / kQm);
+        const float s = f16_bits_to_f32(sb);
+        const float inv = 1.0f / s;
+        uint32_t zb = f32_to_f16_bits(as_f32(-lo * inv));
+        zb = ((zb & 0x7FFFu) == 0x7C00u) ? ((zb & 0x8000u) | 0x7BFFu) : zb;   // overflow -> +-65504
+        const bool zero = (hi == lo);          // constant group
+        p.s = zero ? 0.0f : s;
+        p.inv = zero ? 0.0f : inv;
+        p.zf = zero ? 0.0f : f16_bits_to_f32(zb);
+        p.word = zero ? 0u : (sb | (zb << 16));
+    } else {
+        // symmetric grid about 0, zero point fixed at the middle code
+        constexpr float kQh = (float)((1 << (BITS - 1)) - 1);
+        constexpr float kMid = (float)(1 << (BITS - 1));
+        const uint32_t sb = scale_bits(hi / kQh);
+        const float s = f16_bits_to_f32(sb);
+        const float inv = 1.0f / s;
+        const bool zero = (hi == 0.0f);
+        p.s = zero ? 0.0f : s;
+        p.inv = zero ? 0.0f : inv;
+        p.zf = kMid;
+        p.word = (zero ? 0u : sb) | (f32_to_f16_bits(kMid) << 16);
+    }
     return p;
 }
 
-// code of one value as an integer-valued float: clamp(rint(u/s) + z)
-template <int BITS>
+// code of one value as an integer-valued float
+template <int BITS, int QUANT>
 __device__ __forceinline__ float quant1(float u, const QParams& p)
 {
     constexpr float kQm = (float)((1 << BITS) - 1);
-    return __builtin_amdgcn_fmed3f(__builtin_rintf(u * p.inv) + p.zf, 0.0f, kQm);
+    if constexpr (QUANT == kNaive)   // zero point added before rounding
+        return __builtin_amdgcn_fmed3f(__builtin_rintf(u * p.inv + p.zf), 0.0f, kQm);
+    else                             // integer zero point added after rounding
+        return __builtin_amdgcn_fmed3f(__builtin_rintf(u * p.inv) + p.zf, 0.0f, kQm);
 }
 
 // the 8 codes of a lane, packed (4-bit: one dword, 8-bit: two dwords)
@@ -217,21 +299,29 @@ struct Packed<8> {
     }
 };
 
-// Quantize the lane's 8 values of one group (the whole row cooperates),
-// store codes and parameters, and return the error (q - z) * s - u (or its
-// negation) in e.
-template <int BITS>
-__device__ __forceinline__ void quantize_row(const float* u, bool active, uint32_t l16, int64_t e0,
-                                             uint8_t* codes, uint32_t* params, bool negate, float* e)
+// decode of one parameter word: v = (q - z) * s (the same for every quantizer)
+__device__ __forceinline__ void decode8(const float* q, uint32_t word, float* v)
 {
-    float lo = 0.0f, hi = 0.0f;
+    const float s = f16_bits_to_f32(word & 0xFFFFu);
+    const float zf = f16_bits_to_f32(word >> 16);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { lo = fminf(lo, u[i]); hi = fmaxf(hi, u[i]); }
-    row_minmax(lo, hi);
-    const QParams p = make_params<BITS>(lo, hi);
+    for (int i = 0; i < 8; ++i) v[i] = (q[i] - zf) * s;
+}
+
+// Quantize the lane's 8 values of one group (the whole group cooperates),
+// store codes and parameters, and return the error (q - z) * s - u (or its
+// negation) in e.  `lane` is the lane within the wavefront.
+template <int BITS, int QUANT, int GROUP>
+__device__ __forceinline__ void quantize_group(const float* u, bool active, uint32_t lane, int64_t e0,
+                                               uint8_t* codes, uint32_t* params, bool negate, float* e)
+{
+    float lo, hi;
+    lane_stats<QUANT>(u, lo, hi);
+    group_minmax<GROUP>(lo, hi);
+    const QParams p = make_params<BITS, QUANT>(lo, hi);
     float q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quant1<BITS>(u[i], p);
+    for (int i = 0; i < 8; ++i) q[i] = quant1<BITS, QUANT>(u[i], p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float v = (q[i] - p.zf) * p.s - u[i];
@@ -241,23 +331,23 @@ __device__ __forceinline__ void quantize_row(const float* u, bool active, uint32
     Packed<BITS> pk;
     pk.pack(q);
     pk.store(codes, e0);
-    if (l16 == 0) params[e0 >> 7] = p.word;
+    if ((lane & (GROUP / kEPL - 1)) == 0) params[e0 / GROUP] = p.word;
 }
 
 // Where the lane-contiguous fp32 accesses of a wave land: half h (0/1) of the
 // wave's 512-element chunk covers rows 2h and 2h+1; lane l moves the float4 at
 // offset (4 l) mod 128 of row 2h + l/32.  Rows past the tile re-read the last
-// group (clamped) and are never stored.
+// row (clamped) and are never stored.
 struct WaveMap {
     int64_t seg0;          // first element of the tile in this segment
-    uint32_t gw;           // group index (within the tile) of the wave's row 0
-    uint32_t last;         // tile_groups - 1
+    uint32_t gw;           // row index (within the tile) of the wave's row 0
+    uint32_t last;         // tile_rows - 1
     uint32_t lane;
-    __device__ __forceinline__ uint32_t row_group(uint32_t r) const { return gw + r; }
+    __device__ __forceinline__ uint32_t row(uint32_t r) const { return gw + r; }
     __device__ __forceinline__ int64_t contig(uint32_t h) const
     {
         const uint32_t g = min(gw + 2u * h + (lane >> 5), last);
-        return seg0 + (int64_t)g * kGroup + (int64_t)((4u * lane) & (kGroup - 1));
+        return seg0 + (int64_t)g * kRow + (int64_t)((4u * lane) & (kRow - 1));
     }
     __device__ __forceinline__ bool contig_active(uint32_t h) const { return gw + 2u * h + (lane >> 5) <= last; }
 };
@@ -404,16 +494,16 @@ struct PushArgs {
     float* err;             // nullable, may alias comp
     int64_t S;              // segment length
     int64_t tile_begin;     // tile start inside each segment
-    uint32_t tile_groups;   // groups per segment tile (>= 1)
+    uint32_t tile_rows;     // 128-element rows per segment tile (>= 1)
     int rank;
     int negate;
     UpdArgs upd;            // UPD kernels only: comp is updated in place
 };
 
-// grid: (ceil(tile_groups / (16 U)), P - 1); blockIdx.y = index among the
+// grid: (ceil(tile_rows / (16 U)), P - 1); blockIdx.y = index among the
 // segments this rank does not own.  UPD: comp and upd.slow are required and
 // updated in place (err unused).
-template <int BITS, int U, bool UPD>
+template <int BITS, int U, bool UPD, int QUANT, int GROUP>
 __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
 {
     using Io = Fp32Io<U, UPD>;
@@ -425,7 +515,7 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
     const uint32_t si = blockIdx.y;
     const uint32_t seg = si + (si >= (uint32_t)a.rank ? 1u : 0u);
     const int64_t seg0 = (int64_t)seg * a.S + a.tile_begin;
-    const uint32_t last = a.tile_groups - 1u;
+    const uint32_t last = a.tile_rows - 1u;
     const bool has_comp = UPD || a.comp != nullptr;
     const bool has_out = UPD || a.err != nullptr;
 
@@ -438,16 +528,16 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
         wm[k].gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
         wm[k].last = last;
         wm[k].lane = lane;
-        const int64_t e0 = seg0 + (int64_t)min(wm[k].row_group(rw), last) * kGroup + (int64_t)(l16 * kEPL);
+        const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
         xv[k] = ld_stream((const u32x4*)(a.x + e0));
         if (has_comp) io.load(k, wm[k], e0, a.comp, a.upd.slow);
     }
     if (has_comp) io.stage(lds, wave, lane);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t graw = wm[k].row_group(rw);
+        const uint32_t graw = wm[k].row(rw);
         const bool active = graw <= last;
-        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kGroup + (int64_t)(l16 * kEPL);
+        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kRow + (int64_t)(l16 * kEPL);
         float u[8];
         unpack_bf16x8(xv[k], u);
         if (has_comp) {
@@ -457,7 +547,8 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
             for (int i = 0; i < 8; ++i) u[i] += c[i];
         }
         float e[8];
-        quantize_row<BITS>(u, active, l16, e0, a.codes, a.params, UPD ? false : a.negate != 0, e);
+        quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.codes, a.params,
+                                           UPD ? false : a.negate != 0, e);
         if (UPD) {
             float m[8], cn[8], mn[8];
             io.natural(lds, k, 1, wave, lane, m);
@@ -477,21 +568,23 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
 struct ReduceArgs {
     const uint16_t* x;              // owner's partial sums
     const float* comp;              // owner's compensation, nullable
-    const uint8_t* pc[8];           // push codes of each rank ([owner] unused)
-    const uint32_t* pp[8];          // push parameters of each rank
+    const uint8_t* pc[kMaxP];       // push codes of each rank ([owner] unused)
+    const uint32_t* pp[kMaxP];      // push parameters of each rank
     uint8_t* sc;                    // sum codes (message-shaped)
     uint32_t* sp;                   // sum parameters
     float* err;                     // owner's error, nullable, may alias comp
     int64_t S;
     int64_t tile_begin;
-    uint32_t tile_groups;
+    uint32_t tile_rows;
+    int P;
     int owner;
     int negate;
     UpdArgs upd;                    // UPD kernels only
 };
 
-// grid: (ceil(tile_groups / (16 U)), 1).  UPD as for push_kernel.
-template <int BITS, int P, int U, bool UPD>
+// grid: (ceil(tile_rows / (16 U)), 1).  UPD as for push_kernel.  The peer
+// loop is unrolled to kMaxP with uniform guards on the runtime P.
+template <int BITS, int U, bool UPD, int QUANT, int GROUP>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
 {
     using Io = Fp32Io<U, UPD>;
@@ -501,38 +594,38 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
     const uint32_t l16 = lane & 15u;
     const uint32_t rw = lane >> 4;
     const int64_t seg0 = (int64_t)a.owner * a.S + a.tile_begin;
-    const uint32_t last = a.tile_groups - 1u;
+    const uint32_t last = a.tile_rows - 1u;
     const bool has_comp = UPD || a.comp != nullptr;
     const bool has_out = UPD || a.err != nullptr;
 
     WaveMap wm[U];
     u32x4 xv[U];
     Io io;
-    Packed<BITS> pk[U][P];
-    uint32_t pw[U][P];
+    Packed<BITS> pk[U][kMaxP];
+    uint32_t pw[U][kMaxP];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         wm[k].seg0 = seg0;
         wm[k].gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
         wm[k].last = last;
         wm[k].lane = lane;
-        const int64_t e0 = seg0 + (int64_t)min(wm[k].row_group(rw), last) * kGroup + (int64_t)(l16 * kEPL);
+        const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
         xv[k] = ld_stream((const u32x4*)(a.x + e0));
         if (has_comp) io.load(k, wm[k], e0, a.comp, a.upd.slow);
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            if (j != a.owner) {
+        for (int j = 0; j < kMaxP; ++j) {
+            if (j < a.P && j != a.owner) {
                 pk[k][j].load(a.pc[j], e0);
-                pw[k][j] = a.pp[j][e0 >> 7];
+                pw[k][j] = a.pp[j][e0 / GROUP];
             }
         }
     }
     if (has_comp) io.stage(lds, wave, lane);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t graw = wm[k].row_group(rw);
+        const uint32_t graw = wm[k].row(rw);
         const bool active = graw <= last;
-        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kGroup + (int64_t)(l16 * kEPL);
+        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kRow + (int64_t)(l16 * kEPL);
         float own[8];
         unpack_bf16x8(xv[k], own);
         if (has_comp) {
@@ -544,18 +637,16 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
         // fp32 sum in rank order; the owner's own term enters unquantized
         float acc[8];
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
+        for (int j = 0; j < kMaxP; ++j) {
+            if (j >= a.P) break;
             float t[8];
             if (j == a.owner) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) t[i] = own[i];
             } else {
-                const float s = f16_bits_to_f32(pw[k][j] & 0xFFFFu);
-                const float zf = f16_bits_to_f32(pw[k][j] >> 16);
                 float q[8];
                 pk[k][j].unpack(q);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = (q[i] - zf) * s;
+                decode8(q, pw[k][j], t);
             }
             if (j == 0) {
 #pragma unroll
@@ -566,7 +657,8 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
             }
         }
         float e[8];
-        quantize_row<BITS>(acc, active, l16, e0, a.sc, a.sp, UPD ? false : a.negate != 0, e);
+        quantize_group<BITS, QUANT, GROUP>(acc, active, lane, e0, a.sc, a.sp,
+                                           UPD ? false : a.negate != 0, e);
         if (UPD) {
             float m[8], cn[8], mn[8];
             io.natural(lds, k, 1, wave, lane, m);
@@ -589,11 +681,11 @@ struct GatherArgs {
     void* out;
     int64_t S;
     int64_t tile_begin;
-    uint32_t tile_groups;
+    uint32_t tile_rows;
 };
 
-// grid: (ceil(tile_groups / (16 U)), P); blockIdx.y = segment
-template <int BITS, bool OUT_BF16, int U>
+// grid: (ceil(tile_rows / (16 U)), P); blockIdx.y = segment
+template <int BITS, bool OUT_BF16, int U, int GROUP>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 {
     const uint32_t l16 = threadIdx.x & 15u;
@@ -605,22 +697,19 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
     uint32_t pw[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_groups - 1u);
-        const int64_t e0 = seg0 + (int64_t)gi * kGroup + (int64_t)(l16 * kEPL);
+        const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_rows - 1u);
+        const int64_t e0 = seg0 + (int64_t)gi * kRow + (int64_t)(l16 * kEPL);
         pk[k].load(a.sc, e0);
-        pw[k] = a.sp[e0 >> 7];
+        pw[k] = a.sp[e0 / GROUP];
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
-        if (graw >= a.tile_groups) continue;
-        const int64_t e0 = seg0 + (int64_t)graw * kGroup + (int64_t)(l16 * kEPL);
-        const float s = f16_bits_to_f32(pw[k] & 0xFFFFu);
-        const float zf = f16_bits_to_f32(pw[k] >> 16);
+        if (graw >= a.tile_rows) continue;
+        const int64_t e0 = seg0 + (int64_t)graw * kRow + (int64_t)(l16 * kEPL);
         float q[8], v[8];
         pk[k].unpack(q);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (q[i] - zf) * s;
+        decode8(q, pw[k], v);
         if (OUT_BF16) {
             u32x4 w;
             w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2));

@@ -30,6 +30,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, EINVAL, EALIGN, EUNSUP, ESHAPE, EHIP = 0, -1, -2, -3, -4, -5
 OUT_F32, OUT_BF16 = 0, 1
 ERR_NEGATED = 1
+QUANT_NAIVE, QUANT_SYMMETRIC = 2, 4
+QUANTS = {"zero_aware": 0, "naive": QUANT_NAIVE, "symmetric": QUANT_SYMMETRIC}
 MAX_P = 8
 
 
@@ -46,7 +48,7 @@ class SimArgs(Structure):
     """Mirror of echo_sim_args."""
     _fields_ = [
         ("P", c_int), ("bits", c_int), ("group", c_int), ("tiles", c_int),
-        ("out_dtype", c_int), ("ef", c_int), ("alpha", c_float), ("beta", c_float),
+        ("out_dtype", c_int), ("ef", c_int), ("quant", c_int), ("alpha", c_float), ("beta", c_float),
         ("n", c_int64),
         ("x", c_void_p * MAX_P), ("comp", c_void_p * MAX_P), ("slow", c_void_p * MAX_P),
         ("err", c_void_p * MAX_P), ("out", c_void_p * MAX_P),
@@ -140,11 +142,13 @@ def echo_allreduce_sim_workspace_bytes(P, n, bits, group=128):
 
 
 def make_sim_args(xs, outs, workspace, bits=4, group=128, tiles=1, out_dtype=OUT_F32, ef=False,
-                  alpha=1.0, beta=0.0, comps=None, slows=None, errs=None, workspace_bytes=None):
+                  alpha=1.0, beta=0.0, comps=None, slows=None, errs=None, workspace_bytes=None,
+                  quant="zero_aware"):
     """Fill an echo_sim_args from lists of tensors (one per simulated rank)."""
     P = len(xs)
     a = SimArgs()
     a.P, a.bits, a.group, a.tiles, a.out_dtype, a.ef = P, bits, group, tiles, out_dtype, 1 if ef else 0
+    a.quant = QUANTS[quant]
     a.alpha, a.beta = alpha, beta
     a.n = xs[0].numel() if P else 0
     for r in range(P):

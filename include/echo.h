@@ -34,7 +34,7 @@
  *    S = n / P is the segment length.  Tiles are element ranges *inside each
  *    segment*: [tile_begin, tile_begin + tile_len), both multiples of group,
  *    tile_begin + tile_len <= S.  (0, S) means whole segments.
- *  - bits is 4 or 8; group is 128 (ECHO_EUNSUP otherwise).  P is 1..8.
+ *  - bits is 4 or 8; group is 128 or 256 (ECHO_EUNSUP otherwise).  P is 1..8.
  *  - Codes: unsigned, 0 .. 2^bits - 1.  bits = 4: element i's code is in byte
  *    i/2, the low nibble when i is even; bits = 8: byte i.  Code arrays are
  *    message-shaped: n*bits/8 bytes, segment s at byte offset s*S*bits/8.
@@ -67,8 +67,13 @@ enum echo_status {
 
 enum echo_out_dtype { ECHO_OUT_F32 = 0, ECHO_OUT_BF16 = 1 };
 
-/* flags for echo_quantize_ef / echo_reduce_segment */
-enum { ECHO_ERR_NEGATED = 1 /* write -e (the next call's compensation) instead of e */ };
+/* flags for echo_quantize_ef / echo_reduce_segment (and echo_sim_args.quant
+ * for the two quantizer bits) */
+enum {
+    ECHO_ERR_NEGATED = 1,      /* write -e (the next call's compensation) instead of e */
+    ECHO_QUANT_NAIVE = 2,      /* Table 8 ablation: naive zero point */
+    ECHO_QUANT_SYMMETRIC = 4   /* Table 8 ablation: symmetric grid */
+};
 
 #define ECHO_MAX_P 8
 
@@ -95,6 +100,20 @@ typedef struct echo_qparam {
  *   err = (q - z) * s - u          (or its negation with ECHO_ERR_NEGATED)
  * All float operations are single IEEE fp32 operations (no contraction);
  * 1/s and the scale division are correctly rounded; rint rounds half to even.
+ *
+ * The quantizer above is the full method's (zero-aware asymmetric, Table 8).
+ * The flag bits select one of Table 8's ablations instead (same parameter
+ * word, same decode v = (q - z) * s):
+ *   ECHO_QUANT_NAIVE      lo = min u, hi = max u (no widening to 0);
+ *                         s as above; z = binary16(-lo * (1/s)), a real value
+ *                         (an overflow becomes +-65504); q = clamp(rint(u *
+ *                         (1/s) + z), 0, Qm); hi == lo gives s = +0, z = 0,
+ *                         codes 0.
+ *   ECHO_QUANT_SYMMETRIC  a = max |u|; s = binary16(a / (2^(bits-1) - 1))
+ *                         with the clamps above; z = 2^(bits-1);
+ *                         q = clamp(rint(u * (1/s)) + z, 0, Qm); a == 0 gives
+ *                         s = +0 and all codes z.
+ * Setting both is ECHO_EINVAL.
  *
  *   x_bf16 (device, in)   bfloat16 bits [n] of this rank's partial sums
  *   comp   (device, in)   fp32 [n] compensation, or NULL (no feedback)
@@ -203,10 +222,11 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
 typedef struct echo_sim_args {
     int P;          /* ranks, 1..8 */
     int bits;       /* 4 or 8 */
-    int group;      /* 128 */
+    int group;      /* 128 or 256 */
     int tiles;      /* tiles per segment, >= 1 (capped at S/group) */
     int out_dtype;  /* ECHO_OUT_F32 or ECHO_OUT_BF16 */
     int ef;         /* 0: no compensation; 1: compensation on */
+    int quant;      /* 0 (zero-aware), ECHO_QUANT_NAIVE or ECHO_QUANT_SYMMETRIC */
     float alpha;    /* fast fraction, 0 < alpha <= 1 */
     float beta;     /* slow release rate, 0 <= beta <= 1 */
     int64_t n;      /* elements per rank */

@@ -62,7 +62,7 @@ def test_quantize_ef_argument_checks():
     assert q(tb=1024, tl=128) == echo.ESHAPE          # past the segment end (S = 1024)
     assert q(x=None) == echo.EINVAL and q(codes=None) == echo.EINVAL
     assert q(x=FAKE + 8) == echo.EALIGN and q(comp=FAKE + 4) == echo.EALIGN
-    assert q(flags=2) == echo.EINVAL
+    assert q(flags=8) == echo.EINVAL and q(flags=6) == echo.EINVAL   # unknown bit; both ablations
     assert q(n=1 << 35, P=4) == echo.ESHAPE             # beyond the 2^34 limit
     # empty work is a successful no-op (nothing to enqueue)
     assert q(tl=0) == 0 and q(n=0, tl=0) == 0 and q(P=1, tl=128) == 0
@@ -122,4 +122,7 @@ def test_sim_argument_checks_and_workspace_size():
     assert sim(ef=1, comp=[FAKE] * P, alpha=0.5) == echo.EINVAL             # fused form needs alpha = 1
     assert sim(ef=1, comp=[FAKE] * P, err=[FAKE, None, None, None]) == echo.EINVAL
     assert sim(ef=1, comp=[FAKE] * P, err=[FAKE] * P, alpha=0.5, beta=0.25) == echo.EINVAL  # slow missing
+    assert sim(quant=6) == echo.EINVAL                                      # both ablations
+    assert sim(quant=1) == echo.EINVAL                                      # not a quantizer bit
+    assert sim(group=64) == echo.EUNSUP
     assert sim(n=0) == 0

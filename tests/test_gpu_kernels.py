@@ -240,3 +240,104 @@ def test_quantizer_edge_groups(echo, bits):
     # the scale-tie groups really produced binary16 midpoints and clamps
     sc = wp[0::2]
     assert 0x7BFF in set(sc.tolist()) and 0x0001 in set(sc.tolist())
+
+
+def variant_inputs(P, n, seed):
+    """Partials mixing two-sided, one-sided, near-zero and exact-zero groups,
+    plus a small fp32 compensation, so every quantizer meets its edge cases."""
+    rng = np.random.default_rng(seed)
+    xs = []
+    for r in range(P):
+        v = rng.standard_normal(n).astype(np.float32)
+        blocks = v.reshape(-1, 128)
+        blocks[1::7] = np.abs(blocks[1::7]) + 0.5          # positive, away from 0
+        blocks[2::7] = -np.abs(blocks[2::7])               # non-positive
+        blocks[3::7] *= 1e-3                               # near zero
+        blocks[4::7, ::5] = 0.0                            # exact zeros inside a group
+        blocks[5::11] = 0.0                                # all-zero rows
+        xs.append(oracle.f32_to_bf16_bits(v))
+    comps = [(rng.standard_normal(n) * 0.01).astype(np.float32) for _ in range(P)]
+    return xs, comps
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [128, 256])
+@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric"])
+def test_quantizer_variants_each_step(echo, quant, group, bits):
+    """Table 8's quantizers (full method, naive zero point, symmetric grid) and
+    its group size 256: push, owner reduce and tail decode, step by step, bit
+    for bit against the oracle, on whole segments and a ragged tile."""
+    P = 4
+    n = P * 256 * 19                      # 19 groups of 256 (38 rows) per segment
+    Sn = n // P
+    flag = echo.QUANTS[quant]
+    xs, comps = variant_inputs(P, n, 7 + bits + group)
+    cb = oracle.code_bytes(n, bits)
+    ng = n // group
+    for tb, tl in [(0, Sn), (group, Sn - 3 * group)]:
+        say("variant push", quant, group, bits, tb, tl)
+        pc_h = [np.full(cb, 0x3C, np.uint8) for _ in range(P)]
+        pp_h = [np.full(2 * ng, 0x7777, np.uint16) for _ in range(P)]
+        err_h = [np.full(n, np.float32(-1.5), np.float32) for _ in range(P)]
+        pc_d = [dev_u8(a) for a in pc_h]
+        pp_d = [dev_u16(a) for a in pp_h]
+        err_d = [dev_f32(a) for a in err_h]
+        for r in range(P):
+            oracle.quantize_ef(xs[r], comps[r], n, P, r, tb, tl, bits, group, pc_h[r], pp_h[r], err_h[r], flag)
+            echo.echo_quantize_ef(dev_u16(xs[r]), dev_f32(comps[r]), n, P, r, tb, tl, bits, group, pc_d[r],
+                                  pp_d[r], err_d[r], flag)
+        torch.cuda.synchronize()
+        for r in range(P):
+            assert_bits_equal(host_u8(pc_d[r]), pc_h[r], f"push codes {r}")
+            assert_bits_equal(host_u16(pp_d[r]), pp_h[r], f"push params {r}")
+            assert_bits_equal(host_f32(err_d[r]), err_h[r], f"push err {r}")
+        say("variant reduce", quant, group, bits, tb, tl)
+        sc_h = np.full(cb, 0x11, np.uint8)
+        sp_h = np.full(2 * ng, 0x2222, np.uint16)
+        sc_d, sp_d = dev_u8(sc_h), dev_u16(sp_h)
+        oe_h = [np.full(n, np.float32(2.5), np.float32) for _ in range(P)]
+        oe_d = [dev_f32(a) for a in oe_h]
+        for o in range(P):
+            oracle.reduce_segment(xs[o], comps[o], pc_h, pp_h, P, o, n, tb, tl, bits, group, sc_h, sp_h,
+                                  oe_h[o], flag | oracle.ERR_NEGATED)
+            echo.echo_reduce_segment(dev_u16(xs[o]), dev_f32(comps[o]), pc_d, pp_d, P, o, n, tb, tl, bits,
+                                     group, sc_d, sp_d, oe_d[o], flag | echo.ERR_NEGATED)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u8(sc_d), sc_h, "sum codes")
+        assert_bits_equal(host_u16(sp_d), sp_h, "sum params")
+        for o in range(P):
+            assert_bits_equal(host_f32(oe_d[o]), oe_h[o], f"owner err {o}")
+        for odt in (oracle.OUT_F32, oracle.OUT_BF16):
+            say("variant gather", quant, group, bits, tb, tl, odt)
+            if odt == oracle.OUT_F32:
+                want, out_d = sentinel_f32(n), dev_f32(sentinel_f32(n))
+            else:
+                want, out_d = np.full(n, 0xBEEF, np.uint16), dev_u16(np.full(n, 0xBEEF, np.uint16))
+            oracle.gather_dequant(sc_h, sp_h, n, tb, tl, P, bits, group, want, odt)
+            echo.echo_gather_dequant(sc_d, sp_d, n, tb, tl, P, bits, group, out_d, odt)
+            torch.cuda.synchronize()
+            got = host_f32(out_d) if odt == oracle.OUT_F32 else host_u16(out_d)
+            assert_bits_equal(got, want, "decoded output")
+
+
+@pytest.mark.parametrize("quant", ["naive", "symmetric"])
+def test_quantizer_variant_edge_groups(echo, quant):
+    """The edge groups of the full method's test, through each ablation."""
+    flag = echo.QUANTS[quant]
+    for bits in (4, 8):
+        groups = edge_groups(bits)
+        n = G * len(groups)
+        Sn = n // P
+        comp = np.concatenate(groups).astype(np.float32)
+        x = np.zeros(n, np.uint16)
+        for rank in range(P):
+            say("variant edge groups", quant, bits, rank)
+            cb = oracle.code_bytes(n, bits)
+            wc = np.zeros(cb, np.uint8); wp = np.zeros(2 * n // G, np.uint16); we = np.zeros(n, np.float32)
+            oracle.quantize_ef(x, comp, n, P, rank, 0, Sn, bits, G, wc, wp, we, flag)
+            cd = dev_u8(np.zeros(cb, np.uint8)); pd = params_dev(n // G, 0); ed = dev_f32(np.zeros(n, np.float32))
+            echo.echo_quantize_ef(dev_u16(x), dev_f32(comp), n, P, rank, 0, Sn, bits, G, cd, pd, ed, flag)
+            torch.cuda.synchronize()
+            assert_bits_equal(host_u8(cd), wc, "edge codes")
+            assert_bits_equal(host_u16(pd), wp, "edge params")
+            assert_bits_equal(host_f32(ed), we, "edge err")

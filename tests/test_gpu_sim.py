@@ -26,7 +26,7 @@ MODES = {"off": (1.0, 0.0), "classic": (1.0, 0.0), "classic_unfused": (1.0, 0.0)
          "two_fused": (0.5, 0.25)}
 
 
-def run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams):
+def run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams, quant="zero_aware", group=128):
     """Run len(xs_list) consecutive calls; returns per-call outs and the final state."""
     alpha, beta = MODES[ef_mode]
     ef = ef_mode != "off"
@@ -36,14 +36,14 @@ def run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams):
     slows = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] \
         if ef_mode in ("two", "two_fused") else None
     odtype = torch.float32 if odt == oracle.OUT_F32 else torch.int16
-    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits, group), dtype=torch.uint8, device=DEV)
     streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
     results = []
     for xs in xs_list:
         xd = [dev_u16(x) for x in xs]
         outs = [torch.full((n,), 0x3F, dtype=odtype, device=DEV) for _ in range(P)]
         a = echo.make_sim_args(xd, outs, ws, bits=bits, tiles=tiles, out_dtype=odt, ef=ef, alpha=alpha,
-                               beta=beta, comps=comps, slows=slows, errs=errs)
+                               beta=beta, comps=comps, slows=slows, errs=errs, quant=quant, group=group)
         echo.echo_allreduce_sim(a, streams=streams)
         torch.cuda.synchronize()
         results.append([host_f32(o) if odt == oracle.OUT_F32 else host_u16(o) for o in outs])
@@ -53,7 +53,7 @@ def run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams):
     return results, state
 
 
-def run_oracle_calls(xs_list, P, n, bits, ef_mode, odt):
+def run_oracle_calls(xs_list, P, n, bits, ef_mode, odt, quant="zero_aware", group=128):
     alpha, beta = MODES[ef_mode]
     ef = ef_mode != "off"
     comps = [np.zeros(n, np.float32) for _ in range(P)] if ef else None
@@ -63,8 +63,8 @@ def run_oracle_calls(xs_list, P, n, bits, ef_mode, odt):
     slows = [np.zeros(n, np.float32) for _ in range(P)] if ef_mode in ("two", "two_fused") else None
     results = []
     for xs in xs_list:
-        outs, _, _ = oracle.allreduce(xs, bits=bits, ef=ef, alpha=alpha, beta=beta, comps=comps, slows=slows,
-                                      errs=errs, out_dtype=odt)
+        outs, _, _ = oracle.allreduce(xs, bits=bits, group=group, ef=ef, alpha=alpha, beta=beta, comps=comps,
+                                      slows=slows, errs=errs, out_dtype=odt, quant=quant)
         results.append(outs)
     return results, dict(comps=comps, slows=slows, errs=errs)
 
@@ -109,6 +109,34 @@ def test_sim_matches_oracle_over_calls(echo, P, bits, ef_mode, odt, tiles, nstre
         if wstate[key] is not None and gstate[key] is not None:
             for r in range(P):
                 assert_f32_parity(gstate[key][r], wstate[key][r], f"{key}[{r}]")
+                assert_bits_equal(gstate[key][r], wstate[key][r], f"{key}[{r}] bits")
+
+
+VARIANT_CASES = [
+    # P, bits, ef, out, tiles, streams, quant, group
+    (4, 4, "classic", oracle.OUT_BF16, 3, 4, "naive", 128),
+    (4, 4, "two_fused", oracle.OUT_F32, 1, 1, "symmetric", 128),
+    (4, 4, "classic", oracle.OUT_BF16, 2, 4, "zero_aware", 256),
+    (8, 8, "classic_unfused", oracle.OUT_F32, 3, 2, "naive", 256),
+    (3, 4, "two", oracle.OUT_F32, 2, 3, "symmetric", 256),
+    (2, 8, "off", oracle.OUT_BF16, 1, 1, "naive", 128),
+]
+
+
+@pytest.mark.parametrize("P,bits,ef_mode,odt,tiles,nstreams,quant,group", VARIANT_CASES)
+def test_sim_quantizer_variants_match_oracle(echo, P, bits, ef_mode, odt, tiles, nstreams, quant, group):
+    """Table 8's ablation quantizers and group size through the whole call."""
+    n = P * group * 21
+    xs_list = [[rand_bf16(n, 5000 * c + 10 * P + r, scale=1.0 + c) for r in range(P)] for c in range(3)]
+    say("sim variant", P, bits, ef_mode, odt, tiles, nstreams, quant, group)
+    got, gstate = run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, tiles, nstreams, quant, group)
+    want, wstate = run_oracle_calls(xs_list, P, n, bits, ef_mode, odt, quant, group)
+    for c in range(3):
+        for r in range(P):
+            assert_bits_equal(got[c][r], want[c][r], f"call {c} rank {r} out bits")
+    for key in ("comps", "slows", "errs"):
+        if wstate[key] is not None and gstate[key] is not None:
+            for r in range(P):
                 assert_bits_equal(gstate[key][r], wstate[key][r], f"{key}[{r}] bits")
 
 
