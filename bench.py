@@ -24,6 +24,8 @@ Also printed (same JSON line):
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same
                 workload: 1/32 of every segment's groups, same byte formula.
   staged        the same call with tiles staggered across streams.
+  variants      the same call with Table 8's ablation quantizers (naive zero
+                point, symmetric grid) and with groups of 256.
   p8            the same measurement at P = 8.
 """
 from __future__ import annotations
@@ -52,8 +54,8 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def bytes_per_elem(P, bits, ef, out_bytes):
-    kb = bits / 8 + 4 / G
+def bytes_per_elem(P, bits, ef, out_bytes, group=G):
+    kb = bits / 8 + 4 / group
     return 2 + out_bytes + (8 if ef else 0) + kb * (3 - 1 / P)
 
 
@@ -77,17 +79,19 @@ def committed_traffic(P, tiles, n):
         return None
 
 
-def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, out_bf16, ef, time_kernel=True):
+def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, out_bf16, ef, time_kernel=True,
+             quant="zero_aware", group=G):
     dev = "cuda:0"
     xs = [inputs.laplace(r, n, device=dev) for r in range(P)]
     comps = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if ef else None
     odt = torch.int16 if out_bf16 else torch.float32
     outs = [torch.empty(n, dtype=odt, device=dev) for _ in range(P)]
-    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=dev)
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits, group), dtype=torch.uint8, device=dev)
     main = torch.cuda.current_stream()
     streams = [main] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
-    args = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=tiles,
-                              out_dtype=echo.OUT_BF16 if out_bf16 else echo.OUT_F32, ef=ef, comps=comps)
+    args = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=tiles, group=group,
+                              out_dtype=echo.OUT_BF16 if out_bf16 else echo.OUT_F32, ef=ef, comps=comps,
+                              quant=quant)
     for _ in range(warmup):
         echo.echo_allreduce_sim(args, streams=streams)
     torch.cuda.synchronize()
@@ -103,7 +107,7 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
     ev_ms = ev0.elapsed_time(ev1)
     ms_per_step = max(wall * 1e3, ev_ms) / steps
 
-    B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4)
+    B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4, group)
     value = P * n * B / (ms_per_step * 1e-3) / 1e9
     if not time_kernel:
         del xs, comps, outs, ws
@@ -186,6 +190,8 @@ def main():
     ap.add_argument("--staged-tiles", type=int, default=8)
     ap.add_argument("--staged-streams", type=int, default=4)
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-schedule leg")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the Table 8 quantizer/group-size legs")
     ap.add_argument("--out", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--no-ef", action="store_true")
     ap.add_argument("--no-p8", action="store_true", help="skip the P=8 leg")
@@ -216,6 +222,15 @@ def main():
                       max(5, a.steps // 2), a.warmup, out_bf16, ef, time_kernel=False)
         staged = {"tiles": a.staged_tiles, "streams": a.staged_streams, "value": round(rs["value"], 1),
                   "ms_per_step": round(rs["ms_per_step"], 4), "frac_of_peak": round(rs["value"] / HBM_PEAK_GBS, 4)}
+    variants = None
+    if not a.no_variants:
+        variants = {}
+        for name, quant, group in (("naive_zero_point", "naive", G), ("symmetric_grid", "symmetric", G),
+                                   ("zero_aware_g256", "zero_aware", 256)):
+            rv = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 3),
+                          a.warmup, out_bf16, ef, time_kernel=False, quant=quant, group=group)
+            variants[name] = {"value": round(rv["value"], 1), "ms_per_step": round(rv["ms_per_step"], 4),
+                              "frac_of_peak": round(rv["value"] / HBM_PEAK_GBS, 4)}
     p8 = None
     if not a.no_p8 and a.P != 8:
         r8 = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 2),
@@ -257,6 +272,7 @@ def main():
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "staged": staged,
+        "variants": variants,
         "p8": p8,
     }
     print(json.dumps(line), flush=True)
