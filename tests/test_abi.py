@@ -126,3 +126,19 @@ def test_sim_argument_checks_and_workspace_size():
     assert sim(quant=1) == echo.EINVAL                                      # not a quantizer bit
     assert sim(group=64) == echo.EUNSUP
     assert sim(n=0) == 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/echo.h compiles as strict C99 with gcc, and a C program linked
+    against libecho.so sees the same host-side checks."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "abi_check"
+    lib_dir = os.path.join(root, "error_feedback_quant_amd")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(root, "include"), os.path.join(root, "tests", "c", "abi_check.c"),
+                    "-L", lib_dir, "-l:libecho.so", "-Wl,-rpath," + lib_dir, "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_check: ok" in r.stdout
