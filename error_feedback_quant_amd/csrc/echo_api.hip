@@ -30,7 +30,7 @@ constexpr int64_t kMaxN = int64_t(1) << 34;
 #define ECHO_U_PUSH 2
 #endif
 #ifndef ECHO_U_RED
-#define ECHO_U_RED 1
+#define ECHO_U_RED 2
 #endif
 #ifndef ECHO_U_GATH
 #define ECHO_U_GATH 2
