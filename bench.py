@@ -22,10 +22,16 @@ Also printed (same JSON line):
                 against 8 TB/s; traffic from the committed rocprofv3 counter
                 summary if it was taken on the current kernel source.
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same
-                workload: 1/32 of every segment's groups, same byte formula.
+                workload: 1/4 of every segment's groups, same byte formula.
   staged        the same call with tiles staggered across streams.
   variants      the same call with Table 8's ablation quantizers (naive zero
                 point, symmetric grid) and with groups of 256.
+  modes         the same call with feedback off, with fp32 output, and with
+                the two-timescale compensator fused into push and reduce
+                (B then counts 16 bytes of state traffic instead of 8).
+  config        also carries the per-call median and minimum (HIP events
+                between consecutive calls) and a plain 1 GiB device copy's
+                bandwidth as a measured second denominator.
   p8            the same measurement at P = 8.
 """
 from __future__ import annotations
@@ -54,9 +60,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def bytes_per_elem(P, bits, ef, out_bytes, group=G):
+def bytes_per_elem(P, bits, ef, out_bytes, group=G, two_timescale=False):
+    """Algorithmic bytes per message element per rank.  Classic feedback
+    reads c and writes -e in place (8 B); the two-timescale update, fused into
+    the push and the reduce, reads c and M and writes c' and M' (16 B)."""
     kb = bits / 8 + 4 / group
-    return 2 + out_bytes + (8 if ef else 0) + kb * (3 - 1 / P)
+    state = (16 if two_timescale else 8) if ef else 0
+    return 2 + out_bytes + state + kb * (3 - 1 / P)
 
 
 def push_bytes_per_elem(bits, ef):
@@ -80,10 +90,12 @@ def committed_traffic(P, tiles, n):
 
 
 def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, out_bf16, ef, time_kernel=True,
-             quant="zero_aware", group=G):
+             quant="zero_aware", group=G, alpha=1.0, beta=0.0):
     dev = "cuda:0"
+    two = ef and (alpha != 1.0 or beta != 0.0)
     xs = [inputs.laplace(r, n, device=dev) for r in range(P)]
     comps = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if ef else None
+    slows = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if two else None
     odt = torch.int16 if out_bf16 else torch.float32
     outs = [torch.empty(n, dtype=odt, device=dev) for _ in range(P)]
     ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits, group), dtype=torch.uint8, device=dev)
@@ -91,28 +103,31 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
     streams = [main] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
     args = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=tiles, group=group,
                               out_dtype=echo.OUT_BF16 if out_bf16 else echo.OUT_F32, ef=ef, comps=comps,
-                              quant=quant)
+                              quant=quant, alpha=alpha, beta=beta, slows=slows)
     for _ in range(warmup):
         echo.echo_allreduce_sim(args, streams=streams)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(main)
-    for _ in range(steps):
+    # one event between consecutive calls: per-call times for the median and
+    # the minimum, and the first-to-last span for the whole run
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(main)
+    for i in range(steps):
         echo.echo_allreduce_sim(args, streams=streams)
-    ev1.record(main)
+        evs[i + 1].record(main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
+    ev_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = max(wall * 1e3, ev_ms) / steps
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    call_ms = {"median": round(per_call[steps // 2], 4), "min": round(per_call[0], 4)}
 
-    B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4, group)
+    B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4, group, two)
     value = P * n * B / (ms_per_step * 1e-3) / 1e9
     if not time_kernel:
-        del xs, comps, outs, ws
+        del xs, comps, slows, outs, ws
         torch.cuda.empty_cache()
-        return dict(value=value, ms_per_step=ms_per_step, bytes_per_call=P * n * B, B=B)
+        return dict(value=value, ms_per_step=ms_per_step, bytes_per_call=P * n * B, B=B, call_ms=call_ms)
 
     # dominant kernel: the push of one rank over one tile, timed with events on
     # the stream it is launched on (the sim launches the same kernel, same size)
@@ -148,13 +163,34 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "echo::push_kernel (echo_quantize_ef)", "launch_elements": (P - 1) * tile_len,
             "algorithmic_bytes_per_launch": int(push_bytes), "mean_launch_ms": round(push_ms, 4)}
-    del xs, comps, outs, ws
+    del xs, comps, slows, outs, ws
     torch.cuda.empty_cache()
     return dict(value=value, ms_per_step=ms_per_step, bytes_per_call=P * n * B, B=B, roofline=roof,
-                wall_ms_per_step=wall * 1e3 / steps, event_ms_per_step=ev_ms / steps)
+                wall_ms_per_step=wall * 1e3 / steps, event_ms_per_step=ev_ms / steps, call_ms=call_ms)
 
 
-def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=32):
+def device_copy_gbs(torch, reps=10):
+    """A plain 1 GiB device-to-device copy (hipMemcpyAsync through torch),
+    counted as read + write bytes: a measured second denominator beside the
+    8 TB/s peak."""
+    src = torch.empty(N_1GIB // 2, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * src.numel() * 4 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=4):
     """The oracle (single-threaded C) on a bounded sample of the workload:
     a message 1/frac_den the size (every segment shortened alike), drawn from
     the same Laplace(0,1) recipe, timed over one whole call."""
@@ -194,6 +230,8 @@ def main():
                     help="skip the Table 8 quantizer/group-size legs")
     ap.add_argument("--out", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--no-ef", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the feedback-off, fp32-output and two-timescale legs")
     ap.add_argument("--no-p8", action="store_true", help="skip the P=8 leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
@@ -231,6 +269,21 @@ def main():
                           a.warmup, out_bf16, ef, time_kernel=False, quant=quant, group=group)
             variants[name] = {"value": round(rv["value"], 1), "ms_per_step": round(rv["ms_per_step"], 4),
                               "frac_of_peak": round(rv["value"] / HBM_PEAK_GBS, 4)}
+    modes = None
+    if not a.no_modes:
+        # the same call with feedback off, with fp32 output, and with the
+        # two-timescale compensator (alpha = 0.5, beta = 0.25) fused into the
+        # push and the reduce
+        modes = {}
+        for name, m_ef, m_bf16, alpha, beta in (("ef_off", False, out_bf16, 1.0, 0.0),
+                                                ("f32_out", ef, False, 1.0, 0.0),
+                                                ("two_timescale", True, out_bf16, 0.5, 0.25)):
+            rm = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 3),
+                          a.warmup, m_bf16, m_ef, time_kernel=False, alpha=alpha, beta=beta)
+            modes[name] = {"value": round(rm["value"], 1), "ms_per_step": round(rm["ms_per_step"], 4),
+                           "bytes_per_elem_per_rank": round(rm["B"], 5),
+                           "frac_of_peak": round(rm["value"] / HBM_PEAK_GBS, 4)}
+    copy_gbs = device_copy_gbs(torch)
     p8 = None
     if not a.no_p8 and a.P != 8:
         r8 = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 2),
@@ -268,11 +321,15 @@ def main():
             "out": a.out, "bytes_per_elem_per_rank": round(main_res["B"], 5),
             "bytes_per_call": int(main_res["bytes_per_call"]),
             "frac_of_peak": round(main_res["value"] / HBM_PEAK_GBS, 4),
+            "call_ms": main_res["call_ms"],
+            "device_copy_gbs": round(copy_gbs, 1),
+            "frac_of_device_copy": round(main_res["value"] / copy_gbs, 4),
         },
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "staged": staged,
         "variants": variants,
+        "modes": modes,
         "p8": p8,
     }
     print(json.dumps(line), flush=True)

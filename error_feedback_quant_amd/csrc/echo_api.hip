@@ -38,6 +38,7 @@ constexpr int64_t kMaxN = int64_t(1) << 34;
 constexpr int kUPush = ECHO_U_PUSH;
 constexpr int kURed = ECHO_U_RED;
 constexpr int kUGath = ECHO_U_GATH;
+constexpr size_t kReduceCompLds = 32 * 1024;
 
 int hip_fail(hipError_t e)
 {
@@ -125,7 +126,16 @@ template <int B, bool UP, int Q, int G>
 struct ReduceL {
     static void go(const echo::ReduceArgs& a, dim3 grid, hipStream_t st)
     {
-        hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G>), grid, dim3(echo::kBlock), 0, st, a);
+        // LDS: the staging slices when an fp32 stream is read or written, and
+        // at least kReduceCompLds when the compensation is read.  32 KB holds
+        // residency to five blocks per CU (160 KB of LDS): with the
+        // compensation stream that measured faster than the six that the
+        // registers allow, while the reduce without it wants every wave it
+        // can get and takes no LDS at all.
+        using Io = echo::Fp32Io<kURed, UP>;
+        size_t lds = (UP || a.comp || a.err) ? Io::kLdsFloats * sizeof(float) : 0;
+        if ((UP || a.comp) && lds < kReduceCompLds) lds = kReduceCompLds;
+        hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G>), grid, dim3(echo::kBlock), lds, st, a);
     }
 };
 

@@ -254,11 +254,17 @@ struct Packed;
 template <>
 struct Packed<4> {
     uint32_t w;
+    // q holds integer-valued floats in [0, 15]: the even codes go to the low
+    // nibbles of bytes 0..3 and the odd codes to the high nibbles
     __device__ __forceinline__ void pack(const float* q)
     {
-        w = 0;
+        uint32_t ev = 0, od = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w |= (uint32_t)q[i] << (4 * i);
+        for (int i = 0; i < 4; ++i) {
+            ev = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * i], i, ev);
+            od = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * i + 1], i, od);
+        }
+        w = ev | (od << 4);
     }
     __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
     {
@@ -270,8 +276,15 @@ struct Packed<4> {
     }
     __device__ __forceinline__ void unpack(float* q) const
     {
+        uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+        // opaque to the optimizer, so that each code converts with one
+        // v_cvt_f32_ubyte<i> instead of a bit-field extract and a convert
+        asm volatile("" : "+v"(ev), "+v"(od));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = (float)((w >> (4 * i)) & 0xFu);
+        for (int i = 0; i < 4; ++i) {
+            q[2 * i] = (float)((ev >> (8 * i)) & 0xFFu);
+            q[2 * i + 1] = (float)((od >> (8 * i)) & 0xFFu);
+        }
     }
 };
 template <>
@@ -279,8 +292,14 @@ struct Packed<8> {
     u32x2 w;
     __device__ __forceinline__ void pack(const float* q)
     {
-        w.x = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
-        w.y = (uint32_t)q[4] | ((uint32_t)q[5] << 8) | ((uint32_t)q[6] << 16) | ((uint32_t)q[7] << 24);
+        uint32_t x = 0, y = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x = __builtin_amdgcn_cvt_pk_u8_f32(q[i], i, x);
+            y = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + i], i, y);
+        }
+        w.x = x;
+        w.y = y;
     }
     __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
     {
@@ -309,29 +328,36 @@ __device__ __forceinline__ void decode8(const float* q, uint32_t word, float* v)
 }
 
 // Quantize the lane's 8 values of one group (the whole group cooperates),
-// store codes and parameters, and return the error (q - z) * s - u (or its
-// negation) in e.  `lane` is the lane within the wavefront.
+// store codes and parameters, and return the codes (as integer-valued floats)
+// in q and the group's parameters.  `lane` is the lane within the wavefront.
 template <int BITS, int QUANT, int GROUP>
-__device__ __forceinline__ void quantize_group(const float* u, bool active, uint32_t lane, int64_t e0,
-                                               uint8_t* codes, uint32_t* params, bool negate, float* e)
+__device__ __forceinline__ QParams quantize_group(const float* u, bool active, uint32_t lane, int64_t e0,
+                                                  uint8_t* codes, uint32_t* params, float* q)
 {
     float lo, hi;
     lane_stats<QUANT>(u, lo, hi);
     group_minmax<GROUP>(lo, hi);
     const QParams p = make_params<BITS, QUANT>(lo, hi);
-    float q[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = quant1<BITS, QUANT>(u[i], p);
+    if (active) {
+        Packed<BITS> pk;
+        pk.pack(q);
+        pk.store(codes, e0);
+        if ((lane & (GROUP / kEPL - 1)) == 0) params[e0 / GROUP] = p.word;
+    }
+    return p;
+}
+
+// the quantization error (q - z) * s - u of the lane's 8 values, or its
+// negation; only computed where a kernel writes it out or updates with it
+__device__ __forceinline__ void group_error(const float* q, const QParams& p, const float* u, bool negate, float* e)
+{
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float v = (q[i] - p.zf) * p.s - u[i];
         e[i] = negate ? -v : v;
     }
-    if (!active) return;
-    Packed<BITS> pk;
-    pk.pack(q);
-    pk.store(codes, e0);
-    if ((lane & (GROUP / kEPL - 1)) == 0) params[e0 / GROUP] = p.word;
 }
 
 // Where the lane-contiguous fp32 accesses of a wave land: half h (0/1) of the
@@ -546,10 +572,10 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i) u[i] += c[i];
         }
-        float e[8];
-        quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.codes, a.params,
-                                           UPD ? false : a.negate != 0, e);
+        float q[8], e[8];
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.codes, a.params, q);
         if (UPD) {
+            group_error(q, p, u, false, e);
             float m[8], cn[8], mn[8];
             io.natural(lds, k, 1, wave, lane, m);
 #pragma unroll
@@ -557,6 +583,7 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
             io.put(lds, k, 0, wave, lane, cn, active, (float*)a.comp, e0);
             io.put(lds, k, 1, wave, lane, mn, active, a.upd.slow, e0);
         } else if (has_out) {
+            group_error(q, p, u, a.negate != 0, e);
             io.put(lds, k, 0, wave, lane, e, active, a.err, e0);
         }
     }
@@ -584,11 +611,15 @@ struct ReduceArgs {
 
 // grid: (ceil(tile_rows / (16 U)), 1).  UPD as for push_kernel.  The peer
 // loop is unrolled to kMaxP with uniform guards on the runtime P.
+//
+// LDS is dynamic: the launcher sizes it (at least Io::kLdsFloats floats
+// whenever an fp32 stream is staged), which also sets how many blocks share a
+// CU.
 template <int BITS, int U, bool UPD, int QUANT, int GROUP>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
 {
     using Io = Fp32Io<U, UPD>;
-    __shared__ float lds[Io::kLdsFloats];
+    extern __shared__ float lds[];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = lane & 15u;
@@ -639,27 +670,21 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
 #pragma unroll
         for (int j = 0; j < kMaxP; ++j) {
             if (j >= a.P) break;
-            float t[8];
             if (j == a.owner) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = own[i];
+                for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? own[i] : acc[i] + own[i];
             } else {
-                float q[8];
+                float q[8], t[8];
                 pk[k][j].unpack(q);
                 decode8(q, pw[k][j], t);
-            }
-            if (j == 0) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = t[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = acc[i] + t[i];
+                for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? t[i] : acc[i] + t[i];
             }
         }
-        float e[8];
-        quantize_group<BITS, QUANT, GROUP>(acc, active, lane, e0, a.sc, a.sp,
-                                           UPD ? false : a.negate != 0, e);
+        float q[8], e[8];
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(acc, active, lane, e0, a.sc, a.sp, q);
         if (UPD) {
+            group_error(q, p, acc, false, e);
             float m[8], cn[8], mn[8];
             io.natural(lds, k, 1, wave, lane, m);
 #pragma unroll
@@ -667,6 +692,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
             io.put(lds, k, 0, wave, lane, cn, active, (float*)a.comp, e0);
             io.put(lds, k, 1, wave, lane, mn, active, a.upd.slow, e0);
         } else if (has_out) {
+            group_error(q, p, acc, a.negate != 0, e);
             io.put(lds, k, 0, wave, lane, e, active, a.err, e0);
         }
     }
@@ -684,10 +710,17 @@ struct GatherArgs {
     uint32_t tile_rows;
 };
 
-// grid: (ceil(tile_rows / (16 U)), P); blockIdx.y = segment
+// grid: (ceil(tile_rows / (16 U)), P); blockIdx.y = segment.  bf16 output
+// is already lane-contiguous (16 B per lane, 1 KB per wave); fp32 output (32 B
+// per lane) goes through the wave's LDS slice like the fp32 streams of push
+// and reduce, so that each store instruction writes 1 KB contiguously.
 template <int BITS, bool OUT_BF16, int U, int GROUP>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 {
+    constexpr bool kStageOut = !OUT_BF16 && ECHO_STAGE;
+    __shared__ float lds[kStageOut ? U * (kBlock / 64) * kWaveChunk : 1];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = threadIdx.x & 15u;
     const uint32_t row = threadIdx.x >> 4;
     const int64_t seg0 = (int64_t)blockIdx.y * a.S + a.tile_begin;
@@ -717,10 +750,30 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
             w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
             w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
             st_out((u32x4*)((uint16_t*)a.out + e0), w);
+        } else if (kStageOut) {
+            natural_write(lds + (k * (kBlock / 64) + wave) * kWaveChunk, lane, v);
         } else {
             float* o = (float*)a.out + e0;
             st_out((f32x4*)o, f32x4{v[0], v[1], v[2], v[3]});
             st_out((f32x4*)(o + 4), f32x4{v[4], v[5], v[6], v[7]});
+        }
+    }
+    if constexpr (kStageOut) {
+        // rows past the tile were not decoded and are not stored
+        wave_lds_fence();
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            WaveMap wm;
+            wm.seg0 = seg0;
+            wm.gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
+            wm.last = a.tile_rows - 1u;
+            wm.lane = lane;
+            const float* sl = lds + (k * (kBlock / 64) + wave) * kWaveChunk;
+#pragma unroll
+            for (uint32_t h = 0; h < 2; ++h) {
+                if (!wm.contig_active(h)) continue;
+                st_out((f32x4*)((float*)a.out + wm.contig(h)), *(const f32x4*)(sl + 256 * h + 4 * lane));
+            }
         }
     }
 }
