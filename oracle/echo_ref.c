@@ -205,7 +205,9 @@ static void quant_zero_aware(const float* v, int g, int Qm, uint8_t* q, uint16_t
  *   1. lo = min v, hi = max v (the range is not widened to hold 0).
  *   2. hi == lo: scale +0, zero point 0, codes 0 (the group decodes to 0).
  *   3. s = binary16((hi - lo) / Qm) with the clamps of the full method.
- *   4. inv = 1 / s; z = binary16(-lo * inv), an overflow clamped to +-65504.
+ *   4. inv = 1 / s; z = binary16((0 - lo) * inv), an overflow clamped to
+ *      +-65504.  Written 0 - lo rather than -lo so that a group whose
+ *      minimum is a zero gets z = +0 whichever signed zero the minimum is.
  *   5. q_i = clamp(rint(v_i * inv + z), 0, Qm): the zero point is added
  *      before rounding (two fp32 roundings, then rint).
  * Pinned by: brute force over codes and exact-rational choice of s and z on
@@ -227,7 +229,7 @@ static void quant_naive(const float* v, int g, int Qm, uint8_t* q, uint16_t* sca
     uint16_t sh = scale_bits((hi - lo) / (float)Qm);
     float s = echo_ref_f16_to_f32(sh);
     float inv = 1.0f / s;
-    uint16_t zh = echo_ref_f32_to_f16(-lo * inv);
+    uint16_t zh = echo_ref_f32_to_f16((0.0f - lo) * inv);
     if ((zh & 0x7FFFu) == 0x7C00u) zh = (uint16_t)((zh & 0x8000u) | 0x7BFFu);
     float zf = echo_ref_f16_to_f32(zh);
     for (int i = 0; i < g; ++i) q[i] = clamp_code((double)rintf(v[i] * inv + zf), Qm);
