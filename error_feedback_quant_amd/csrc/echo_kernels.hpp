@@ -99,28 +99,50 @@ __device__ __forceinline__ void wave_lds_fence()
     __builtin_amdgcn_wave_barrier();
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v)
+// A value moved across lanes by DPP is an integer to the compiler; a float
+// min/max of it first re-canonicalizes it (one more instruction per step).
+// The group reduction therefore works on integer keys with the order of the
+// floats (finite values; -0 sorts below +0), and the move folds into
+// v_min_i32_dpp / v_max_i32_dpp.  The key map is its own inverse.
+__device__ __forceinline__ int order_key(float f)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    const int b = __builtin_bit_cast(int, f);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float from_order_key(int k)
+{
+    return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+
+// Every lane has a valid source under the four patterns used here (quad_perm
+// and row_ror stay inside a 16-lane row) and every lane of the wave is active
+// where the group reduction runs, so bound_ctrl's zero fill never applies; it
+// lets the backend fold the move into the consuming min/max.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 // min and max over the lanes of a group (16 lanes, or 32 for GROUP = 256);
-// every lane ends with the result
+// every lane ends with the result.  Only the sign of a zero result can differ
+// from a sequential min/max, and no quantizer's output depends on it.
 template <int GROUP>
 __device__ __forceinline__ void group_minmax(float& lo, float& hi)
 {
-    lo = fminf(lo, dpp_f<0xB1>(lo));  hi = fmaxf(hi, dpp_f<0xB1>(hi));   // quad_perm [1,0,3,2]
-    lo = fminf(lo, dpp_f<0x4E>(lo));  hi = fmaxf(hi, dpp_f<0x4E>(hi));   // quad_perm [2,3,0,1]
-    lo = fminf(lo, dpp_f<0x124>(lo)); hi = fmaxf(hi, dpp_f<0x124>(hi));  // row_ror:4
-    lo = fminf(lo, dpp_f<0x128>(lo)); hi = fmaxf(hi, dpp_f<0x128>(hi));  // row_ror:8
+    int l = order_key(lo), h = order_key(hi);
+    l = min(l, dpp_i<0xB1>(l));  h = max(h, dpp_i<0xB1>(h));    // quad_perm [1,0,3,2]
+    l = min(l, dpp_i<0x4E>(l));  h = max(h, dpp_i<0x4E>(h));    // quad_perm [2,3,0,1]
+    l = min(l, dpp_i<0x124>(l)); h = max(h, dpp_i<0x124>(h));   // row_ror:4
+    l = min(l, dpp_i<0x128>(l)); h = max(h, dpp_i<0x128>(h));   // row_ror:8
     if constexpr (GROUP == 256) {
         // rows 0<->1 and 2<->3: ds_swizzle in swap-16 mode hands every lane
         // the value of lane ^ 16 (through the LDS crossbar, no LDS memory)
-        lo = fminf(lo, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, lo), 0x401F)));
-        hi = fmaxf(hi, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, hi), 0x401F)));
+        l = min(l, __builtin_amdgcn_ds_swizzle(l, 0x401F));
+        h = max(h, __builtin_amdgcn_ds_swizzle(h, 0x401F));
     }
+    lo = from_order_key(l);
+    hi = from_order_key(h);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -214,7 +236,10 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         const uint32_t sb = scale_bits((hi - lo) / kQm);
         const float s = f16_bits_to_f32(sb);
         const float inv = 1.0f / s;
-        uint32_t zb = f32_to_f16_bits(as_f32(-lo * inv));
+        // 0 - lo, not -lo: +0 for a zero minimum.  Pinned in a register, as
+        // the backend otherwise turns (0 - lo) * inv into (-lo) * inv.
+        const float nlo = as_f32(0.0f - lo);
+        uint32_t zb = f32_to_f16_bits(as_f32(nlo * inv));
         zb = ((zb & 0x7FFFu) == 0x7C00u) ? ((zb & 0x8000u) | 0x7BFFu) : zb;   // overflow -> +-65504
         const bool zero = (hi == lo);          // constant group
         p.s = zero ? 0.0f : s;
@@ -616,7 +641,7 @@ struct ReduceArgs {
 // whenever an fp32 stream is staged), which also sets how many blocks share a
 // CU.
 template <int BITS, int U, bool UPD, int QUANT, int GROUP>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(const ReduceArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 4 && !UPD ? 6 : 1))) void reduce_kernel(const ReduceArgs a)
 {
     using Io = Fp32Io<U, UPD>;
     extern __shared__ float lds[];
