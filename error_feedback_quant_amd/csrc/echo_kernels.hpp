@@ -214,6 +214,26 @@ __device__ __forceinline__ void lane_stats(const float* u, float& lo, float& hi)
     }
 }
 
+// x / Q, correctly rounded, for x >= 0 and the quantizers' constant
+// divisors Q = 15, 255 (2^b - 1) and 7, 127 (2^(b-1) - 1), without a
+// division: q0 = x * RN(1/Q); the remainder x - q0 * Q is exact by fma; the
+// quotient is q0 + r * RN(1/Q), rounded once.  For these four Q the result
+// equals IEEE x / Q for every finite x >= 0, subnormals included (checked
+// over all 2^31 inputs on the host).  An infinite x would give NaN, so the
+// range is first clamped at 2^100: every quotient above 65520 rounds to the
+// same binary16 infinity, which the scale clamp turns into 65504.
+template <int Q>
+__device__ __forceinline__ float div_by_const(float x)
+{
+    constexpr float kInv = 1.0f / (float)Q;
+    x = fminf(x, 0x1p100f);
+    const float q0 = x * kInv;
+    const float r = __builtin_fmaf(-q0, (float)Q, x);
+    // the fp32 quotient is kept as such: the backend would otherwise fuse the
+    // last fma with the binary16 conversion (v_fma_mixlo_f16, one rounding)
+    return as_f32(__builtin_fmaf(r, kInv, q0));
+}
+
 template <int BITS, int QUANT>
 __device__ __forceinline__ QParams make_params(float lo, float hi)
 {
@@ -221,7 +241,7 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
     QParams p;
     if constexpr (QUANT == kZeroAware) {
         // range holds 0; integer zero point, so 0 is exactly code z
-        const uint32_t sb = scale_bits((hi - lo) / kQm);
+        const uint32_t sb = scale_bits(div_by_const<(1 << BITS) - 1>(hi - lo));
         const float s = f16_bits_to_f32(sb);
         const float inv = 1.0f / s;
         const float zr = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * inv), 0.0f, kQm);
@@ -233,7 +253,7 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         p.word = zero ? 0u : (sb | (f32_to_f16_bits(zf) << 16));
     } else if constexpr (QUANT == kNaive) {
         // plain min/max range; real-valued zero point -lo/s in binary16
-        const uint32_t sb = scale_bits((hi - lo) / kQm);
+        const uint32_t sb = scale_bits(div_by_const<(1 << BITS) - 1>(hi - lo));
         const float s = f16_bits_to_f32(sb);
         const float inv = 1.0f / s;
         // 0 - lo, not -lo: +0 for a zero minimum.  Pinned in a register, as
@@ -248,9 +268,8 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         p.word = zero ? 0u : (sb | (zb << 16));
     } else {
         // symmetric grid about 0, zero point fixed at the middle code
-        constexpr float kQh = (float)((1 << (BITS - 1)) - 1);
         constexpr float kMid = (float)(1 << (BITS - 1));
-        const uint32_t sb = scale_bits(hi / kQh);
+        const uint32_t sb = scale_bits(div_by_const<(1 << (BITS - 1)) - 1>(hi));
         const float s = f16_bits_to_f32(sb);
         const float inv = 1.0f / s;
         const bool zero = (hi == 0.0f);

@@ -1,0 +1,29 @@
+"""Host checks of arithmetic identities the HIP kernels rely on (CPU only).
+
+The quantizers' scale is s32 = x / Q for a constant Q (2^b - 1 for the
+zero-aware and naive quantizers, 2^(b-1) - 1 for the symmetric grid).  The
+kernels compute it without a division, as q0 = x * RN(1/Q), r = fma(-q0, Q, x),
+q = fma(r, RN(1/Q), q0).  tests/c/div_by_const_check.c checks, over every
+finite fp32 x >= 0, that q is the IEEE quotient for Q = 15, 255, 7 and 127,
+and that the plain product q0 is not (so the check can tell them apart).
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_division_free_quotient_is_exact_for_every_input(tmp_path):
+    exe = tmp_path / "div_by_const_check"
+    subprocess.run(["gcc", "-O3", "-march=native", "-fopenmp", "-ffp-contract=off", "-o", str(exe),
+                    os.path.join(HERE, "c", "div_by_const_check.c"), "-lm"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    lines = r.stdout.strip().splitlines()
+    assert len(lines) == 4
+    for line in lines:
+        assert "mismatches=0 " in line, line
