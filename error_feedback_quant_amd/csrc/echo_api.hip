@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "echo.h"
+#include "echo_gemm.hpp"
 #include "echo_kernels.hpp"
 
 namespace {
@@ -317,6 +318,48 @@ int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P
         return ECHO_EALIGN;
     return launch_push(x_bf16, comp, n, P, rank, tile_begin, tile_len, bits, group, codes, params, err,
                        flags, nullptr, (hipStream_t)stream);
+}
+
+int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,
+                          int64_t K, const float* comp, int P, int rank, int bits, int group,
+                          uint8_t* codes, echo_qparam* params, float* err, uint16_t* x_out,
+                          int flags, void* stream)
+{
+    if (P < 1 || P > ECHO_MAX_P) return ECHO_EINVAL;
+    if (bits != 4 && bits != 8) return ECHO_EUNSUP;
+    if (group != echo::kGBN) return ECHO_EUNSUP;
+    if (M < 0 || N < 0 || K < 0) return ECHO_ESHAPE;
+    if (N % echo::kGBN || M % ((int64_t)echo::kGBM * P)) return ECHO_ESHAPE;
+    if (M != 0 && N != 0 && (K == 0 || K % echo::kGBK)) return ECHO_ESHAPE;
+    if (N != 0 && M > kMaxN / N) return ECHO_ESHAPE;
+    if (rank < 0 || rank >= P) return ECHO_EINVAL;
+    if ((flags & ~(kKnownFlags | ECHO_X_ALL)) || quant_of(flags) < 0) return ECHO_EINVAL;
+    if (M == 0 || N == 0) return ECHO_OK;
+    if (!a_bf16 || !w_bf16 || !codes || !params || !x_out) return ECHO_EINVAL;
+    if (!aligned16(a_bf16) || !aligned16(w_bf16) || !aligned16(codes) || !aligned16(params) ||
+        !aligned16(x_out) || (comp && !aligned16(comp)) || (err && !aligned16(err)))
+        return ECHO_EALIGN;
+    echo::GemmPushArgs g;
+    g.a = a_bf16; g.w = w_bf16; g.comp = comp; g.codes = codes; g.params = (uint32_t*)params;
+    g.err = err; g.x_out = x_out;
+    g.M = M; g.N = N; g.K = K; g.seg_rows = M / P;
+    g.tiles_m = (uint32_t)(M / echo::kGBM); g.tiles_n = (uint32_t)(N / echo::kGBN);
+    g.rank = rank; g.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0; g.x_all = (flags & ECHO_X_ALL) ? 1 : 0;
+    const dim3 grid(g.tiles_m * g.tiles_n);
+    const hipStream_t st = (hipStream_t)stream;
+    const int q = quant_of(flags);
+#define ECHO_GEMM_GO(B, Q) hipLaunchKernelGGL((echo::gemm_push_kernel<B, Q>), grid, dim3(256), 0, st, g)
+    if (bits == 4) {
+        if (q == echo::kZeroAware) ECHO_GEMM_GO(4, echo::kZeroAware);
+        else if (q == echo::kNaive) ECHO_GEMM_GO(4, echo::kNaive);
+        else ECHO_GEMM_GO(4, echo::kSymmetric);
+    } else {
+        if (q == echo::kZeroAware) ECHO_GEMM_GO(8, echo::kZeroAware);
+        else if (q == echo::kNaive) ECHO_GEMM_GO(8, echo::kNaive);
+        else ECHO_GEMM_GO(8, echo::kSymmetric);
+    }
+#undef ECHO_GEMM_GO
+    return check_launch();
 }
 
 int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,

@@ -31,6 +31,7 @@ OK, EINVAL, EALIGN, EUNSUP, ESHAPE, EHIP = 0, -1, -2, -3, -4, -5
 OUT_F32, OUT_BF16 = 0, 1
 ERR_NEGATED = 1
 QUANT_NAIVE, QUANT_SYMMETRIC = 2, 4
+X_ALL = 8
 QUANTS = {"zero_aware": 0, "naive": QUANT_NAIVE, "symmetric": QUANT_SYMMETRIC}
 MAX_P = 8
 
@@ -71,6 +72,9 @@ _lib.echo_gather_dequant.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int
                                      c_void_p, c_int, c_void_p]
 _lib.echo_compensate.restype = c_int
 _lib.echo_compensate.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_float, c_float, c_void_p]
+_lib.echo_gemm_quantize_ef.restype = c_int
+_lib.echo_gemm_quantize_ef.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int,
+                                       c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p]
 _lib.echo_allreduce_sim_workspace_bytes.restype = c_size_t
 _lib.echo_allreduce_sim_workspace_bytes.argtypes = [c_int, c_int64, c_int, c_int]
 _lib.echo_allreduce_sim.restype = c_int
@@ -114,6 +118,13 @@ def echo_quantize_ef(x, comp, n, P, rank, tile_begin, tile_len, bits, group, cod
     _check("echo_quantize_ef", _lib.echo_quantize_ef(
         _ptr(x), _ptr(comp), n, P, rank, tile_begin, tile_len, bits, group, _ptr(codes), _ptr(params),
         _ptr(err), flags, _stream(stream)))
+
+
+def echo_gemm_quantize_ef(a, w, M, N, K, comp, P, rank, bits, group, codes, params, err, x_out, flags=0,
+                          stream=None):
+    _check("echo_gemm_quantize_ef", _lib.echo_gemm_quantize_ef(
+        _ptr(a), _ptr(w), M, N, K, _ptr(comp), P, rank, bits, group, _ptr(codes), _ptr(params), _ptr(err),
+        _ptr(x_out), flags, _stream(stream)))
 
 
 def echo_reduce_segment(own_x, own_comp, peer_codes, peer_params, P, owner, n, tile_begin, tile_len, bits,

@@ -21,9 +21,16 @@ a tensor-parallel block would produce):
   training  P=4, 32 x 4096 x 1024 per rank, 28 layers x 2 sites, forward then
             backward; forward N(0,1); backward N(0, 1e-3) with 0.05 % of the
             elements multiplied by 50.
+  tpblock   the operands of one rank's row-parallel matmul, A [M, K] and
+            W [N, K] in bf16: "normal" draws activations N(0,1) and weights
+            N(0, 1/K) (random init, so the partial sums have unit scale);
+            "int" draws small integers (A in [-4, 4], W in [-3, 3]), whose
+            products and sums are exact in fp32 at any summation order.
+            Default shape: a Llama-3-8B MLP down projection at TP = 4 (4096
+            tokens, hidden 4096, K = 14336 / 4 = 3584).
 
 Seed of (workload, step, site, rank): 20261202 + 1000003*w + 10007*step +
-101*site + rank, with w = 1..5 in the order above.
+101*site + rank, with w = 1..6 in the order above.
 """
 from __future__ import annotations
 
@@ -31,7 +38,7 @@ import math
 
 import torch
 
-WORKLOADS = {"single": 1, "chain": 2, "onegb": 3, "chain8": 4, "training": 5}
+WORKLOADS = {"single": 1, "chain": 2, "onegb": 3, "chain8": 4, "training": 5, "tpblock": 6}
 
 SHAPES = {
     "single": dict(P=4, tokens=64, hidden=1024, bits=4, sites=1),
@@ -39,6 +46,7 @@ SHAPES = {
     "onegb": dict(P=4, tokens=1, hidden=1 << 29, bits=4, sites=1),
     "chain8": dict(P=4, tokens=4096, hidden=1024, bits=8, sites=56),
     "training": dict(P=4, tokens=32 * 4096, hidden=1024, bits=4, sites=56),
+    "tpblock": dict(P=4, tokens=4096, hidden=4096, bits=4, sites=1, k=14336 // 4),
 }
 
 
@@ -128,6 +136,21 @@ def laplace_from_uniform(u: torch.Tensor) -> torch.Tensor:
     """Laplace(0, 1) from U[0, 1) draws by inversion, finite for every draw."""
     c = u - 0.5
     return -torch.sign(c) * torch.log1p(-2.0 * c.abs().clamp(max=_HALF_BELOW))
+
+
+def tp_operands(rank: int, M: int, N: int, K: int, kind: str = "normal", site: int = 0, device="cpu"):
+    """A [M, K] and W [N, K] (bf16 bit tensors, int16) of one rank's
+    row-parallel matmul; see the module docstring."""
+    g = _gen(seed_of("tpblock", 0, site, rank), device=device)
+    if kind == "int":
+        a = torch.randint(-4, 5, (M, K), generator=g, device=device).to(torch.float32)
+        w = torch.randint(-3, 4, (N, K), generator=g, device=device).to(torch.float32)
+    elif kind == "normal":
+        a = torch.randn(M, K, generator=g, dtype=torch.float32, device=device)
+        w = torch.randn(N, K, generator=g, dtype=torch.float32, device=device) * (1.0 / math.sqrt(K))
+    else:
+        raise ValueError(kind)
+    return _bf16_bits(a), _bf16_bits(w)
 
 
 def as_numpy_u16(t: torch.Tensor):

@@ -67,12 +67,13 @@ enum echo_status {
 
 enum echo_out_dtype { ECHO_OUT_F32 = 0, ECHO_OUT_BF16 = 1 };
 
-/* flags for echo_quantize_ef / echo_reduce_segment (and echo_sim_args.quant
- * for the two quantizer bits) */
+/* flags for echo_quantize_ef / echo_reduce_segment / echo_gemm_quantize_ef
+ * (and echo_sim_args.quant for the two quantizer bits) */
 enum {
     ECHO_ERR_NEGATED = 1,      /* write -e (the next call's compensation) instead of e */
     ECHO_QUANT_NAIVE = 2,      /* Table 8 ablation: naive zero point */
-    ECHO_QUANT_SYMMETRIC = 4   /* Table 8 ablation: symmetric grid */
+    ECHO_QUANT_SYMMETRIC = 4,  /* Table 8 ablation: symmetric grid */
+    ECHO_X_ALL = 8             /* echo_gemm_quantize_ef only: write x for every segment */
 };
 
 #define ECHO_MAX_P 8
@@ -105,8 +106,9 @@ typedef struct echo_qparam {
  * The flag bits select one of Table 8's ablations instead (same parameter
  * word, same decode v = (q - z) * s):
  *   ECHO_QUANT_NAIVE      lo = min u, hi = max u (no widening to 0);
- *                         s as above; z = binary16(-lo * (1/s)), a real value
- *                         (an overflow becomes +-65504); q = clamp(rint(u *
+ *                         s as above; z = binary16((0 - lo) * (1/s)), a real
+ *                         value (+0 when the minimum is a zero of either sign;
+ *                         an overflow becomes +-65504); q = clamp(rint(u *
  *                         (1/s) + z), 0, Qm); hi == lo gives s = +0, z = 0,
  *                         codes 0.
  *   ECHO_QUANT_SYMMETRIC  a = max |u|; s = binary16(a / (2^(bits-1) - 1))
@@ -190,6 +192,45 @@ int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params,
  */
 int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
                     float alpha, float beta, void* stream);
+
+/*
+ * echo_gemm_quantize_ef — one rank's row-parallel matmul with the entry pass
+ * and push quantization fused into its epilogue.  Paper card Fig. 2(a) (each
+ * rank quantizes its partial sums for the segments it does not own);
+ * article "The cancellation rule" (the compensator is folded into the entry
+ * pass, beside the matmul, without changing the computed values).
+ *
+ * Computes this rank's partial sums x = bf16(A W^T), i.e.
+ *   x[m*N + j] = bfloat16(sum_k A[m][k] * W[j][k])   (fp32 accumulation,
+ *                                                     round to nearest even)
+ * and then does exactly what echo_quantize_ef(x, comp, M*N, P, rank, 0,
+ * M*N/P, bits, group, codes, params, err, flags) does, without writing x for
+ * the pushed segments: the message is x in row-major order, segment s is
+ * rows [s*M/P, (s+1)*M/P), one group is 128 consecutive columns of a row.
+ * The rank's own segment of x is written to x_out (bf16), for the owner
+ * reduce; with ECHO_X_ALL, x_out receives every segment.  The fp32 sum order
+ * is the kernel's own (K in steps of 16, MFMA accumulation), so x matches a
+ * separate GEMM only up to fp32 rounding of the sum; everything after x is
+ * bit-exact.
+ *
+ *   a_bf16 (device, in)   bfloat16 bits [M][K], row-major (K contiguous)
+ *   w_bf16 (device, in)   bfloat16 bits [N][K], row-major (K contiguous): the
+ *                         weight of y = a w^T
+ *   comp   (device, in)   fp32 [M*N] compensation, or NULL (no feedback)
+ *   codes, params, err    as for echo_quantize_ef (message-shaped; err may
+ *                         alias comp or be NULL)
+ *   x_out  (device, out)  bfloat16 bits [M*N]; rows of segment `rank` (all
+ *                         rows with ECHO_X_ALL) are written, others untouched
+ * Constraints: group == 128 (ECHO_EUNSUP otherwise); N a multiple of 128, K
+ * a positive multiple of 64, M a multiple of 128*P, M*N <= 2^34
+ * (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those of
+ * echo_quantize_ef and ECHO_X_ALL.
+ * Pointers as for echo_quantize_ef, plus a_bf16, w_bf16 and x_out required.
+ */
+int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,
+                          int64_t K, const float* comp, int P, int rank, int bits, int group,
+                          uint8_t* codes, echo_qparam* params, float* err, uint16_t* x_out,
+                          int flags, void* stream);
 
 /*
  * echo_allreduce_sim — one whole call for P simulated ranks: push, owner

@@ -35,6 +35,7 @@ LIB = os.path.join(HERE, "libecho_ref.so")
 OK, EINVAL, EUNSUP, ESHAPE = 0, -1, -3, -4
 ERR_NEGATED = 1
 Q_NAIVE, Q_SYMMETRIC = 2, 4          # quantizer flag bits (Table 8 ablations)
+X_ALL = 8                            # gemm_quantize_ef: x_out receives every segment
 QUANTS = {"zero_aware": 0, "naive": Q_NAIVE, "symmetric": Q_SYMMETRIC}
 OUT_F32, OUT_BF16 = 0, 1
 
@@ -179,6 +180,41 @@ def quantize_ef(x, comp, n, P, rank, tile_begin, tile_len, bits, group, codes, p
         _need(err, np.float32, n)
     _check("quantize_ef", lib().echo_ref_quantize_ef(_p(x), _p(comp), n, P, rank, tile_begin, tile_len,
                                                      bits, group, _p(codes), _p(params), _p(err), flags))
+
+
+# --- the matmul that produces a rank's partial sums -----------------------------
+
+def bf16_bits_to_f32(x) -> np.ndarray:
+    return (np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def matmul_bf16(a, w) -> np.ndarray:
+    """A rank's partial sums x = bfloat16(A W^T) of a row-parallel linear
+    layer (the message of the all-reduce, paper card Fig. 2(a)): A [M, K] and
+    W [N, K] are bf16 bit arrays; the products and their sum are taken in
+    float64 (a library matmul), then rounded to fp32 and to bf16 (nearest
+    even).  Returns the row-major message, uint16 [M*N]."""
+    a64 = bf16_bits_to_f32(a).astype(np.float64)
+    w64 = bf16_bits_to_f32(w).astype(np.float64)
+    return f32_to_bf16_bits((a64 @ w64.T).astype(np.float32)).reshape(-1)
+
+
+def gemm_quantize_ef(a, w, comp, P, rank, bits, codes, params, err, x_out, flags=0, x=None):
+    """The fused matmul + entry pass as its two steps: x = matmul_bf16(A, W)
+    (or the given x), then quantize_ef over the whole message (segment s =
+    rows [s*M/P, (s+1)*M/P)); the rank's own rows of x go to x_out (every row
+    with X_ALL).  Returns x."""
+    M, N = a.shape[0], w.shape[0]
+    n = M * N
+    if x is None:
+        x = matmul_bf16(a, w)
+    quantize_ef(x, comp, n, P, rank, 0, n // P, bits, 128, codes, params, err, flags & ~X_ALL)
+    if flags & X_ALL:
+        x_out[:] = x
+    else:
+        S = n // P
+        x_out[rank * S:(rank + 1) * S] = x[rank * S:(rank + 1) * S]
+    return x
 
 
 def reduce_segment(own_x, own_comp, peer_codes, peer_params, P, owner, n, tile_begin, tile_len, bits,

@@ -11,8 +11,8 @@ from error_feedback_quant_amd import echo
 def test_every_declared_function_is_exported():
     names = echo.declared_functions()
     expected = {"echo_quantize_ef", "echo_reduce_segment", "echo_gather_dequant", "echo_compensate",
-                "echo_allreduce_sim", "echo_allreduce_sim_workspace_bytes", "echo_status_str",
-                "echo_last_hip_error"}
+                "echo_gemm_quantize_ef", "echo_allreduce_sim", "echo_allreduce_sim_workspace_bytes",
+                "echo_status_str", "echo_last_hip_error"}
     assert expected <= set(names), names
     L = echo.lib()
     for nm in names:
@@ -66,6 +66,27 @@ def test_quantize_ef_argument_checks():
     assert q(n=1 << 35, P=4) == echo.ESHAPE             # beyond the 2^34 limit
     # empty work is a successful no-op (nothing to enqueue)
     assert q(tl=0) == 0 and q(n=0, tl=0) == 0 and q(P=1, tl=128) == 0
+
+
+def test_gemm_quantize_ef_argument_checks():
+    M, N, K, P = 512, 256, 128, 4
+    g = lambda **kw: rc_of(echo.echo_gemm_quantize_ef, kw.get("a", FAKE), kw.get("w", FAKE), kw.get("M", M),
+                           kw.get("N", N), kw.get("K", K), kw.get("comp", None), kw.get("P", P),
+                           kw.get("rank", 0), kw.get("bits", 4), kw.get("group", 128), kw.get("codes", FAKE),
+                           kw.get("params", FAKE), kw.get("err", None), kw.get("x_out", FAKE),
+                           kw.get("flags", 0), stream=0)
+    assert g(bits=2) == echo.EUNSUP and g(group=256) == echo.EUNSUP
+    assert g(P=0) == echo.EINVAL and g(P=9) == echo.EINVAL and g(rank=4) == echo.EINVAL
+    assert g(N=N + 64) == echo.ESHAPE                 # N not a multiple of 128
+    assert g(K=K + 32) == echo.ESHAPE and g(K=0) == echo.ESHAPE
+    assert g(M=384) == echo.ESHAPE                    # M not a multiple of 128 * P
+    assert g(M=-128) == echo.ESHAPE
+    assert g(M=1 << 22, N=1 << 13) == echo.ESHAPE     # M * N beyond 2^34
+    assert g(a=None) == echo.EINVAL and g(w=None) == echo.EINVAL and g(x_out=None) == echo.EINVAL
+    assert g(codes=None) == echo.EINVAL
+    assert g(a=FAKE + 2) == echo.EALIGN and g(err=FAKE + 4) == echo.EALIGN
+    assert g(flags=16) == echo.EINVAL and g(flags=6) == echo.EINVAL
+    assert g(M=0) == 0 and g(N=0) == 0                # nothing to compute
 
 
 def test_reduce_gather_compensate_argument_checks():

@@ -1,0 +1,150 @@
+"""GPU parity of echo_gemm_quantize_ef (row-parallel matmul with the entry
+pass and push quantization fused into its epilogue) against the oracle.
+
+* Integer-valued operands (A in [-4, 4], W in [-3, 3]): every product and
+  partial sum is exact in fp32, so x is the same at any summation order and
+  every output is compared bit for bit: x (own rows; all rows with
+  ECHO_X_ALL; untouched rows keep a sentinel), codes, parameters and the
+  error.  Shapes span several tiles in M and N, several K steps, P = 1, 2, 4
+  and 8, both bit widths, the three quantizers, feedback on and off, the
+  negated error written in place over the compensation.
+* Normal operands (activations N(0,1), weights N(0,1/K)): the kernel's fp32
+  sum order differs from the oracle's float64 sum, so x is checked against
+  the bound of fp32 accumulation plus one bf16 rounding; then the oracle's
+  push applied to the kernel's own x must reproduce the codes, parameters
+  and errors bit for bit (the epilogue is exactly the push step).
+* The Llama-3-8B MLP down projection at TP = 4 (M = N = 4096, K = 3584), the
+  shape the benchmark times, on the normal operands, same checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import assert_bits_equal, dev_f32, dev_u8, dev_u16, host_f32, host_u8, host_u16, params_dev, say
+from error_feedback_quant_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0xBEEF
+
+
+@pytest.fixture(scope="module")
+def echo():
+    from error_feedback_quant_amd import echo as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def operands(rank, M, N, K, kind, site=0):
+    a, w = inputs.tp_operands(rank, M, N, K, kind, site=site)
+    return inputs.as_numpy_u16(a).reshape(M, K), inputs.as_numpy_u16(w).reshape(N, K)
+
+
+def run_gpu(echo, a, w, comp, P, rank, bits, flags, with_err, err_in_place):
+    M, K = a.shape
+    N = w.shape[0]
+    n = M * N
+    cd = dev_u8(np.zeros(oracle.code_bytes(n, bits), np.uint8))
+    pd = params_dev(n // 128, 0)
+    comp_d = dev_f32(comp) if comp is not None else None
+    if err_in_place:
+        err_d = comp_d
+    elif with_err:
+        err_d = dev_f32(np.full(n, 7.0, np.float32))
+    else:
+        err_d = None
+    x_d = dev_u16(np.full(n, SENT, np.uint16))
+    echo.echo_gemm_quantize_ef(dev_u16(a), dev_u16(w), M, N, K, comp_d, P, rank, bits, 128, cd, pd, err_d,
+                               x_d, flags)
+    torch.cuda.synchronize()
+    return (host_u8(cd), host_u16(pd), host_f32(err_d) if err_d is not None else None, host_u16(x_d))
+
+
+def run_oracle(a, w, comp, P, rank, bits, flags, with_err, err_in_place, x=None):
+    M, N = a.shape[0], w.shape[0]
+    n = M * N
+    codes = np.zeros(oracle.code_bytes(n, bits), np.uint8)
+    params = np.zeros(2 * n // 128, np.uint16)
+    comp_h = comp.copy() if comp is not None else None
+    if err_in_place:
+        err = comp_h
+    elif with_err:
+        err = np.full(n, 7.0, np.float32)
+    else:
+        err = None
+    x_out = np.full(n, SENT, np.uint16)
+    x = oracle.gemm_quantize_ef(a, w, comp_h, P, rank, bits, codes, params, err, x_out, flags, x=x)
+    return codes, params, err, x_out, x
+
+
+INT_CASES = [
+    # M, N, K, P, bits, quant, mode
+    (512, 256, 128, 4, 4, "zero_aware", "negated_in_place"),
+    (512, 256, 128, 4, 8, "zero_aware", "err"),
+    (512, 384, 192, 4, 4, "naive", "comp_only"),
+    (256, 256, 64, 2, 4, "symmetric", "negated_in_place"),
+    (1024, 128, 320, 8, 8, "naive", "negated_in_place"),
+    (1024, 256, 128, 8, 4, "zero_aware", "plain"),
+    (128, 256, 256, 1, 4, "zero_aware", "err"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,P,bits,quant,mode", INT_CASES)
+def test_fused_gemm_push_exact_operands(echo, M, N, K, P, bits, quant, mode):
+    flags = echo.QUANTS[quant] | (echo.ERR_NEGATED if mode == "negated_in_place" else 0)
+    comp = None
+    if mode in ("negated_in_place", "err", "comp_only"):
+        comp = (np.random.default_rng(M + N + K).standard_normal(M * N) * 2.0).astype(np.float32)
+    with_err = mode in ("err", "plain")
+    in_place = mode == "negated_in_place"
+    for rank in sorted({0, P - 1, P // 2}):
+        for x_all in (0, echo.X_ALL):
+            say("gemm exact", M, N, K, P, bits, quant, mode, rank, x_all)
+            a, w = operands(rank, M, N, K, "int")
+            got = run_gpu(echo, a, w, comp, P, rank, bits, flags | x_all, with_err, in_place)
+            want = run_oracle(a, w, comp, P, rank, bits, flags | x_all, with_err, in_place)
+            assert_bits_equal(got[3], want[3], "x_out")
+            assert_bits_equal(got[0], want[0], "codes")
+            assert_bits_equal(got[1], want[1], "params")
+            if want[2] is not None:
+                assert_bits_equal(got[2], want[2], "err")
+
+
+def check_normal(echo, M, N, K, P, rank, bits, flags):
+    a, w = operands(rank, M, N, K, "normal")
+    n = M * N
+    comp = (np.random.default_rng(n + rank).standard_normal(n) * 0.05).astype(np.float32)
+    got = run_gpu(echo, a, w, comp, P, rank, bits, flags | echo.X_ALL, False, True)
+    x_gpu = got[3]
+    # x against the float64 sum: fp32 accumulation of K products adds at most
+    # about K * 2^-24 of sum |a w|, then one bf16 rounding (half an ulp, 2^-9
+    # relative) on each side
+    a64 = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w64 = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = (a64 @ w64.T).reshape(-1)
+    mag = (np.abs(a64) @ np.abs(w64).T).reshape(-1)
+    xg = (x_gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(exact) + K * 2.0 ** -23 * mag + 2.0 ** -133
+    bad = np.abs(xg - exact) > bound
+    assert not bad.any(), f"x: {int(bad.sum())} of {n} outside the accumulation bound"
+    x_ref = oracle.matmul_bf16(a, w)
+    assert np.mean(x_ref == x_gpu) > 0.95          # almost all sums round alike
+    # everything after x is exactly the push step on the kernel's own x
+    want = run_oracle(a, w, comp, P, rank, bits, flags | echo.X_ALL, False, True, x=x_gpu)
+    assert_bits_equal(got[0], want[0], "codes")
+    assert_bits_equal(got[1], want[1], "params")
+    assert_bits_equal(got[2], want[2], "err (negated, in place)")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_fused_gemm_push_normal_operands(echo, bits):
+    say("gemm normal", bits)
+    check_normal(echo, 512, 512, 512, 4, 2, bits, echo.ERR_NEGATED)
+
+
+def test_fused_gemm_push_llama_down_projection(echo):
+    shp = inputs.SHAPES["tpblock"]
+    M, N, K, P = shp["tokens"], shp["hidden"], shp["k"], shp["P"]
+    say("gemm llama down-proj", M, N, K, P)
+    check_normal(echo, M, N, K, P, 1, 4, echo.ERR_NEGATED)
