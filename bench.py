@@ -29,6 +29,11 @@ Also printed (same JSON line):
   modes         the same call with feedback off, with fp32 output, and with
                 the two-timescale compensator fused into push and reduce
                 (B then counts 16 bytes of state traffic instead of 8).
+  tp_block      one rank's row-parallel matmul with the entry pass fused in
+                its epilogue (echo_gemm_quantize_ef) against hipBLASLt +
+                echo_quantize_ef, at the Llama-3-8B down projection (TP = 4),
+                with an MFMA roofline; and the two-timescale update run
+                beside the next matmul against back to back.
   config        also carries the per-call median and minimum (HIP events
                 between consecutive calls) and a plain 1 GiB device copy's
                 bandwidth as a measured second denominator.
@@ -169,6 +174,93 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
                 wall_ms_per_step=wall * 1e3 / steps, event_ms_per_step=ev_ms / steps, call_ms=call_ms)
 
 
+def tp_block(echo, torch, inputs, reps=10):
+    """One rank's row-parallel matmul and entry pass at the Llama-3-8B MLP down
+    projection with TP = 4 (4096 tokens, hidden 4096, K = 14336/4), random
+    weights: the fused echo_gemm_quantize_ef against torch.matmul (hipBLASLt)
+    followed by echo_quantize_ef, same compensation and outputs; and the
+    two-timescale update (echo_compensate) run beside the next matmul (the
+    gate/up projection, N = 2*14336/4) on a second stream, against running
+    the two back to back."""
+    shp = inputs.SHAPES["tpblock"]
+    M, N, K, P = shp["tokens"], shp["hidden"], shp["k"], shp["P"]
+    n = M * N
+    dev = "cuda:0"
+    a16, w16 = inputs.tp_operands(1, M, N, K, "normal", device=dev)
+    comp = torch.zeros(n, dtype=torch.float32, device=dev)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    params = torch.empty(2 * n // 128, dtype=torch.int16, device=dev)
+    x_out = torch.empty(n, dtype=torch.int16, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    main = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        for _ in range(reps):
+            fn()
+        e1.record(main)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3          # microseconds
+
+    fused = lambda: echo.echo_gemm_quantize_ef(a16, w16, M, N, K, comp, P, 1, 4, 128, codes, params, comp,
+                                               x_out, echo.ERR_NEGATED, stream=main)
+    gemm_only = lambda: echo.echo_gemm_quantize_ef(a16, w16, M, N, K, None, 1, 0, 4, 128, codes, params, None,
+                                                   x_out, 0, stream=main)
+    lib = lambda: torch.matmul(a16.view(torch.bfloat16), w16.view(torch.bfloat16).t(), out=y)
+    push = lambda: echo.echo_quantize_ef(y.view(torch.int16), comp, n, P, 1, 0, n // P, 4, 128, codes, params,
+                                         comp, echo.ERR_NEGATED, stream=main)
+    t_fused = timed(fused)
+    t_gemm = timed(gemm_only)
+    t_lib = timed(lib)
+    t_lib_push = timed(lambda: (lib(), push()))
+    flop = 2.0 * M * N * K
+
+    N2 = 2 * 14336 // P
+    w2 = (torch.randn(N2, N, device=dev) * N ** -0.5).to(torch.bfloat16)
+    z = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+    err = torch.randn(n, device=dev) * 1e-2
+    slow = torch.zeros(n, device=dev)
+    side = torch.cuda.Stream()
+    nxt = lambda: torch.matmul(y, w2.t(), out=z)
+    upd = lambda s: echo.echo_compensate(err, comp, slow, n, 0.5, 0.25, stream=s)
+
+    def beside():
+        ev = torch.cuda.Event()
+        ev.record(main)
+        side.wait_event(ev)
+        nxt()
+        upd(side)
+        ev2 = torch.cuda.Event()
+        ev2.record(side)
+        main.wait_event(ev2)
+
+    t_next = timed(nxt)
+    t_upd = timed(lambda: upd(main))
+    t_serial = timed(lambda: (nxt(), upd(main)))
+    t_beside = timed(beside)
+    out = {
+        "shape": {"M": M, "N": N, "K": K, "P": P, "bits": 4, "ef": "classic, -e in place"},
+        "fused_us": round(t_fused, 1),
+        "gemm_alone_us": round(t_gemm, 1),
+        "hipblaslt_gemm_us": round(t_lib, 1),
+        "hipblaslt_gemm_plus_push_us": round(t_lib_push, 1),
+        "roofline": {"bound": "mfma", "achieved": round(flop / t_fused / 1e6, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(flop / t_fused / 1e6 / 2500.0, 4),
+                     "kernel": "echo::gemm256_push_kernel (echo_gemm_quantize_ef)"},
+        "gemm_alone_tflops": round(flop / t_gemm / 1e6, 1),
+        "hipblaslt_tflops": round(flop / t_lib / 1e6, 1),
+        "update_beside_next_matmul": {"next_matmul_us": round(t_next, 1), "update_us": round(t_upd, 1),
+                                      "serial_us": round(t_serial, 1), "beside_us": round(t_beside, 1)},
+    }
+    del a16, w16, comp, codes, params, x_out, y, w2, z, err, slow
+    torch.cuda.empty_cache()
+    return out
+
+
 def device_copy_gbs(torch, reps=10):
     """A plain 1 GiB device-to-device copy (hipMemcpyAsync through torch),
     counted as read + write bytes: a measured second denominator beside the
@@ -233,6 +325,7 @@ def main():
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the feedback-off, fp32-output and two-timescale legs")
     ap.add_argument("--no-p8", action="store_true", help="skip the P=8 leg")
+    ap.add_argument("--no-tp", action="store_true", help="skip the fused matmul + entry pass leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
@@ -284,6 +377,7 @@ def main():
                            "bytes_per_elem_per_rank": round(rm["B"], 5),
                            "frac_of_peak": round(rm["value"] / HBM_PEAK_GBS, 4)}
     copy_gbs = device_copy_gbs(torch)
+    tp = None if a.no_tp else tp_block(echo, torch, inputs)
     p8 = None
     if not a.no_p8 and a.P != 8:
         r8 = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 2),
@@ -331,6 +425,7 @@ def main():
         "variants": variants,
         "modes": modes,
         "p8": p8,
+        "tp_block": tp,
     }
     print(json.dumps(line), flush=True)
 

@@ -59,10 +59,20 @@ struct GemmPushArgs {
     int x_all;
 };
 
-// byte offset of 16-byte chunk c of tile row r in a stage buffer
+// Byte offset of 16-byte chunk c of tile row r in a stage buffer.  A row is
+// 128 B, so without a swizzle every row of an operand fragment (one row per
+// lane) would start on the same bank.  The chunk is XORed with
+// (r mod 8) ^ ((r / 8) mod 2): any 8 consecutive rows then use 8 distinct
+// chunk positions, and so do the 8 even and the 8 odd rows of any aligned
+// group of 16, which keeps a 16-lane phase of ds_read_b128 on distinct banks
+// whether the LDS serves 8 lanes x 16 B or 16 lanes x 16 B per clock.
+__device__ __forceinline__ uint32_t gemm_swz_key(uint32_t r)
+{
+    return (r & 7u) ^ ((r >> 3) & 1u);
+}
 __device__ __forceinline__ uint32_t gemm_swz(uint32_t r, uint32_t c)
 {
-    return (r * kGChunks + (c ^ (r & 7u))) * 16u;
+    return (r * kGChunks + (c ^ gemm_swz_key(r))) * 16u;
 }
 
 // tile of linear block b: each XCD (b mod 8) takes a contiguous range of a
@@ -192,6 +202,157 @@ __global__ __launch_bounds__(256) void gemm_push_kernel(const GemmPushArgs a)
             st_stream((u32x4*)(a.x_out + e0), w);
         }
         if (own) continue;                     // uniform over the block
+        if (has_comp) {
+            const f32x4 c0 = ld_stream((const f32x4*)(a.comp + e0));
+            const f32x4 c1 = ld_stream((const f32x4*)(a.comp + e0 + 4));
+            u[0] += c0.x; u[1] += c0.y; u[2] += c0.z; u[3] += c0.w;
+            u[4] += c1.x; u[5] += c1.y; u[6] += c1.z; u[7] += c1.w;
+        }
+        float q[8];
+        const QParams prm = quantize_group<BITS, QUANT, kGBN>(u, true, lane, e0, a.codes, a.params, q);
+        if (a.err) {
+            float e[8];
+            group_error(q, prm, u, a.negate != 0, e);
+            st_stream((f32x4*)(a.err + e0), f32x4{e[0], e[1], e[2], e[3]});
+            st_stream((f32x4*)(a.err + e0 + 4), f32x4{e[4], e[5], e[6], e[7]});
+        }
+    }
+}
+
+
+// ------------------------------------------------ 256 x 256 tiles, 8 waves --
+//
+// Same computation on 256 x 256 tiles: 512 threads as 2 x 4 wavefronts of
+// 128 x 64 outputs (4 x 2 MFMA tiles, 128 accumulators per lane), so each
+// 16-deep step reads 6 operand fragments from LDS for 8 MFMAs.  Stages are
+// filled with global_load_lds_dwordx4: one instruction of a wavefront moves 8
+// rows x 128 B and lane i lands at the wave-uniform base + 16 i, i.e. row
+// i / 8, physical chunk i % 8; the lane therefore fetches the logical chunk
+// that the XOR swizzle puts there.  Two 64 KB stages, 128 KB of LDS; the
+// epilogue reuses it for the bf16 tile.
+constexpr int kG2BM = 256;
+constexpr int kG2BN = 256;
+constexpr int kG2Threads = 512;
+constexpr int kG2StageBytes = (kG2BM + kG2BN) * kGBK * 2;
+
+__device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint8_t* lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+template <int BITS, int QUANT>
+__global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm256_push_kernel(const GemmPushArgs a)
+{
+    __shared__ __align__(16) uint8_t smem[2 * kG2StageBytes];   // 128 KB
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = tid >> 6;
+    const uint32_t wm = wave >> 2, wn = wave & 3u;
+    uint32_t tm, tn;
+    gemm_tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kG2BM, n0 = (int64_t)tn * kG2BN;
+
+    // this lane's share of a stage: rows wave*8 + 64 i + lane/8 (i = 0..3) of
+    // A and of W, lane % 8 is the physical chunk, so it fetches the logical
+    // chunk (lane % 8) ^ key(row); key(row) is the same for every i
+    const uint32_t lrow = lane >> 3;
+    const uint32_t lchunk = (lane & 7u) ^ gemm_swz_key(wave * 8 + lrow);
+    const uint16_t* ga = a.a + (m0 + wave * 8 + lrow) * a.K + 8 * lchunk;
+    const uint16_t* gw = a.w + (n0 + wave * 8 + lrow) * a.K + 8 * lchunk;
+    const int64_t row64 = 64 * a.K;
+    auto issue = [&](int buf, int64_t k0) {
+        uint8_t* sa = smem + buf * kG2StageBytes;
+        uint8_t* sw = sa + kG2BM * kGBK * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t r0 = wave * 8 + 64 * i;
+            gemm_load_lds16(ga + i * row64 + k0, sa + r0 * (kGChunks * 16));
+            gemm_load_lds16(gw + i * row64 + k0, sw + r0 * (kGChunks * 16));
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    const int64_t KT = a.K / kGBK;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const uint32_t orow = lane & 31u, ohalf = lane >> 5;
+    for (int64_t kt = 0; kt < KT; ++kt) {
+        const int buf = (int)(kt & 1);
+        if (kt + 1 < KT) issue(buf ^ 1, (kt + 1) * kGBK);
+        const uint8_t* sa = smem + buf * kG2StageBytes;
+        const uint8_t* sw = sa + kG2BM * kGBK * 2;
+        // Software pipeline over the four 16-deep steps: the fragments of
+        // step kk + 2 are read while the MFMAs of step kk run, so at most 12
+        // LDS reads are in flight (the LDS counter waits on at most 15) and
+        // the MFMAs of a step wait only for that step's six reads.  The
+        // scheduling barriers keep the compiler from sinking each read to its
+        // use, which would serialize LDS latency with the MFMAs.
+        bf16x8 fa[4][4], fb[4][2];
+        auto read_step = [&](uint32_t kk) {
+            const uint32_t c = 2 * kk + ohalf;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[kk][i] = *(const bf16x8*)(sa + gemm_swz(wm * 128 + 32 * i + orow, c));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fb[kk][j] = *(const bf16x8*)(sw + gemm_swz(wn * 64 + 32 * j + orow, c));
+        };
+        auto mfma_step = [&](uint32_t kk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+        };
+        read_step(0);
+        read_step(1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(0);
+        read_step(2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(1);
+        read_step(3);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(3);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the next stage has landed
+        __syncthreads();
+    }
+
+    // ---- epilogue: x = bf16(acc) as a [256][256] tile in LDS, then the push
+    // step on 16 rows (32 groups) per pass
+    uint16_t* xt = (uint16_t*)smem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const uint32_t r = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * ohalf + (v & 3);
+                const uint32_t col = wn * 64 + 32 * j + orow;
+                xt[r * kG2BN + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+            }
+    __syncthreads();
+
+    const uint32_t l16 = tid & 15u;
+    const uint32_t gcol = ((tid >> 4) & 1u) * kGBN + kEPL * l16;
+    const bool has_comp = a.comp != nullptr;
+    for (uint32_t p = 0; p < kG2BM / 16; ++p) {
+        const uint32_t r = p * 16 + (tid >> 5);
+        const int64_t grow = m0 + r;
+        const bool own = grow / a.seg_rows == a.rank;   // uniform: segments hold whole 16-row passes
+        const int64_t e0 = grow * a.N + n0 + gcol;
+        const u32x4 xw = *(const u32x4*)(xt + r * kG2BN + gcol);
+        if (own || a.x_all) st_stream((u32x4*)(a.x_out + e0), xw);
+        if (own) continue;
+        float u[8];
+        unpack_bf16x8(xw, u);
         if (has_comp) {
             const f32x4 c0 = ld_stream((const f32x4*)(a.comp + e0));
             const f32x4 c1 = ld_stream((const f32x4*)(a.comp + e0 + 4));

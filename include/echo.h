@@ -221,10 +221,10 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  *                         alias comp or be NULL)
  *   x_out  (device, out)  bfloat16 bits [M*N]; rows of segment `rank` (all
  *                         rows with ECHO_X_ALL) are written, others untouched
- * Constraints: group == 128 (ECHO_EUNSUP otherwise); N a multiple of 128, K
- * a positive multiple of 64, M a multiple of 128*P, M*N <= 2^34
- * (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those of
- * echo_quantize_ef and ECHO_X_ALL.
+ * Constraints: group == 128 (ECHO_EUNSUP otherwise); M and N multiples of
+ * 256, K a positive multiple of 64, M a multiple of P with M/P a multiple of
+ * 16, M*N <= 2^34 (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those
+ * of echo_quantize_ef and ECHO_X_ALL.
  * Pointers as for echo_quantize_ef, plus a_bf16, w_bf16 and x_out required.
  */
 int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,

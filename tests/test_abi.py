@@ -77,9 +77,10 @@ def test_gemm_quantize_ef_argument_checks():
                            kw.get("flags", 0), stream=0)
     assert g(bits=2) == echo.EUNSUP and g(group=256) == echo.EUNSUP
     assert g(P=0) == echo.EINVAL and g(P=9) == echo.EINVAL and g(rank=4) == echo.EINVAL
-    assert g(N=N + 64) == echo.ESHAPE                 # N not a multiple of 128
+    assert g(N=N + 128) == echo.ESHAPE                # N not a multiple of 256
     assert g(K=K + 32) == echo.ESHAPE and g(K=0) == echo.ESHAPE
-    assert g(M=384) == echo.ESHAPE                    # M not a multiple of 128 * P
+    assert g(M=384) == echo.ESHAPE                    # M not a multiple of 256
+    assert g(M=256, P=3) == echo.ESHAPE               # M not a multiple of P
     assert g(M=-128) == echo.ESHAPE
     assert g(M=1 << 22, N=1 << 13) == echo.ESHAPE     # M * N beyond 2^34
     assert g(a=None) == echo.EINVAL and g(w=None) == echo.EINVAL and g(x_out=None) == echo.EINVAL

@@ -81,12 +81,14 @@ def run_oracle(a, w, comp, P, rank, bits, flags, with_err, err_in_place, x=None)
 INT_CASES = [
     # M, N, K, P, bits, quant, mode
     (512, 256, 128, 4, 4, "zero_aware", "negated_in_place"),
-    (512, 256, 128, 4, 8, "zero_aware", "err"),
-    (512, 384, 192, 4, 4, "naive", "comp_only"),
+    (512, 512, 128, 4, 8, "zero_aware", "err"),
+    (512, 768, 192, 4, 4, "naive", "comp_only"),
     (256, 256, 64, 2, 4, "symmetric", "negated_in_place"),
-    (1024, 128, 320, 8, 8, "naive", "negated_in_place"),
-    (1024, 256, 128, 8, 4, "zero_aware", "plain"),
-    (128, 256, 256, 1, 4, "zero_aware", "err"),
+    (1024, 256, 320, 8, 8, "naive", "negated_in_place"),
+    (1024, 512, 128, 8, 4, "zero_aware", "plain"),
+    (512, 256, 128, 8, 4, "zero_aware", "negated_in_place"),   # 64-row segments: 4 per tile
+    (768, 256, 64, 3, 4, "symmetric", "err"),
+    (256, 256, 256, 1, 4, "zero_aware", "err"),
 ]
 
 
