@@ -40,9 +40,6 @@ constexpr int kUPush = ECHO_U_PUSH;
 constexpr int kURed = ECHO_U_RED;
 constexpr int kUGath = ECHO_U_GATH;
 constexpr size_t kReduceCompLds = 32 * 1024;
-#ifndef ECHO_GEMM_BIG
-#define ECHO_GEMM_BIG 1
-#endif
 
 int hip_fail(hipError_t e)
 {
@@ -330,13 +327,9 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
 {
     if (P < 1 || P > ECHO_MAX_P) return ECHO_EINVAL;
     if (bits != 4 && bits != 8) return ECHO_EUNSUP;
-    if (group != echo::kGBN) return ECHO_EUNSUP;
+    if (group != echo::kGGroup) return ECHO_EUNSUP;   // one group = 128 columns of a row
     if (M < 0 || N < 0 || K < 0) return ECHO_ESHAPE;
-#if ECHO_GEMM_BIG
-    if (N % echo::kG2BN || M % echo::kG2BM || M % P || (M / P) % 16) return ECHO_ESHAPE;
-#else
-    if (N % echo::kGBN || M % ((int64_t)echo::kGBM * P)) return ECHO_ESHAPE;
-#endif
+    if (N % echo::kGTile || M % echo::kGTile || M % P || (M / P) % 16) return ECHO_ESHAPE;
     if (M != 0 && N != 0 && (K == 0 || K % echo::kGBK)) return ECHO_ESHAPE;
     if (N != 0 && M > kMaxN / N) return ECHO_ESHAPE;
     if (rank < 0 || rank >= P) return ECHO_EINVAL;
@@ -353,15 +346,9 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
     g.rank = rank; g.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0; g.x_all = (flags & ECHO_X_ALL) ? 1 : 0;
     const hipStream_t st = (hipStream_t)stream;
     const int q = quant_of(flags);
-#if ECHO_GEMM_BIG
-    g.tiles_m = (uint32_t)(M / echo::kG2BM); g.tiles_n = (uint32_t)(N / echo::kG2BN);
+    g.tiles_m = (uint32_t)(M / echo::kGTile); g.tiles_n = (uint32_t)(N / echo::kGTile);
     const dim3 grid(g.tiles_m * g.tiles_n);
-#define ECHO_GEMM_GO(B, Q) hipLaunchKernelGGL((echo::gemm256_push_kernel<B, Q>), grid, dim3(echo::kG2Threads), 0, st, g)
-#else
-    g.tiles_m = (uint32_t)(M / echo::kGBM); g.tiles_n = (uint32_t)(N / echo::kGBN);
-    const dim3 grid(g.tiles_m * g.tiles_n);
-#define ECHO_GEMM_GO(B, Q) hipLaunchKernelGGL((echo::gemm_push_kernel<B, Q>), grid, dim3(256), 0, st, g)
-#endif
+#define ECHO_GEMM_GO(B, Q) hipLaunchKernelGGL((echo::gemm256_push_kernel<B, Q>), grid, dim3(echo::kGThreads), 0, st, g)
     if (bits == 4) {
         if (q == echo::kZeroAware) ECHO_GEMM_GO(4, echo::kZeroAware);
         else if (q == echo::kNaive) ECHO_GEMM_GO(4, echo::kNaive);

@@ -10,8 +10,8 @@
 //
 // One launch computes one rank's partial sums X = A W^T (A: M x K, W: N x K,
 // both bf16 with K contiguous, fp32 accumulation), rounds them to bf16 and,
-// instead of writing X and reading it back, runs the push step on each 128 x
-// 128 output tile while it is still on chip:
+// instead of writing X and reading it back, runs the push step on each 256 x
+// 256 output tile while it is still on chip:
 //   * rows of the rank's own segment: X (bf16) is written out, for the owner
 //     reduce;
 //   * every other row: u = f32(x) + c, one quantization group per 128
@@ -20,24 +20,28 @@
 // The values are those of "GEMM to bf16, then echo_quantize_ef" for the same
 // accumulation; only the HBM round trip of X for the pushed segments is gone.
 //
-// Main loop: 256 threads (2 x 2 wavefronts, 64 x 64 outputs each) per
-// 128 x 128 tile, K in steps of 64, v_mfma_f32_32x32x16_bf16 (2 x 2 per
-// wavefront per 16-deep step).  Tiles of A and W are staged through LDS in two
-// buffers; 16-byte chunks are XOR-swizzled by row so that the 32 rows read by
-// one MFMA operand load spread over the LDS banks.  The tile order is
-// XCD-aware: the 8 XCDs each take a compact block of tiles, so that the A and
-// W panels a tile needs are shared in that XCD's L2.
+// Main loop: 512 threads per 256 x 256 tile as 2 x 4 wavefronts of 128 x 64
+// outputs (4 x 2 tiles of v_mfma_f32_32x32x16_bf16, 128 accumulators per
+// lane), K in stages of 64, so each 16-deep step reads 6 operand fragments
+// from LDS for 8 MFMAs.  Stages are filled with global_load_lds_dwordx4: one
+// instruction of a wavefront moves 8 rows x 128 B and lane i lands at the
+// wave-uniform base + 16 i (row i / 8, physical chunk i % 8), so the lane
+// fetches the logical chunk that the XOR swizzle puts there.  Two 64 KB
+// stages, 128 KB of LDS; the epilogue reuses it for the bf16 tile.  The tile
+// order is XCD-aware: the 8 XCDs each take a compact block of tiles, so that
+// the A and W panels a tile needs are shared in that XCD's L2.
 #pragma once
 
 #include "echo_kernels.hpp"
 
 namespace echo {
 
-constexpr int kGBM = 128;   // tile rows (M)
-constexpr int kGBN = 128;   // tile columns (N) = one quantization group per row
-constexpr int kGBK = 64;    // K per stage
-constexpr int kGChunks = kGBK / 8;                     // 16-byte chunks per tile row
-constexpr int kGStageBytes = (kGBM + kGBN) * kGBK * 2; // A + W, one stage
+constexpr int kGTile = 256;                            // tile rows = tile columns
+constexpr int kGGroup = 128;                           // columns of one quantization group
+constexpr int kGBK = 64;                               // K per stage
+constexpr int kGThreads = 512;                         // 8 wavefronts
+constexpr int kGChunks = kGBK / 8;                     // 16-byte chunks per stage row
+constexpr int kGStageBytes = 2 * kGTile * kGBK * 2;    // A + W, one stage (64 KB)
 constexpr int kGXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,7 +56,7 @@ struct GemmPushArgs {
     float* err;             // [M*N], nullable, may alias comp
     uint16_t* x_out;        // [M*N] bf16: own segment (and every segment if x_all)
     int64_t M, N, K;
-    int64_t seg_rows;       // rows per segment (M / P), a multiple of kGBM
+    int64_t seg_rows;       // rows per segment (M / P), a multiple of 16
     uint32_t tiles_m, tiles_n;
     int rank;
     int negate;
@@ -91,150 +95,6 @@ __device__ __forceinline__ void gemm_tile_of(uint32_t b, uint32_t tm_n, uint32_t
     tn = in / rows;
 }
 
-template <int BITS, int QUANT>
-__global__ __launch_bounds__(256) void gemm_push_kernel(const GemmPushArgs a)
-{
-    __shared__ __align__(16) uint8_t smem[2 * kGStageBytes];   // 64 KB; the epilogue reuses it
-    const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & 63u;
-    const uint32_t wave = tid >> 6;
-    const uint32_t wm = wave >> 1, wn = wave & 1u;
-    uint32_t tm, tn;
-    gemm_tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kGBM, n0 = (int64_t)tn * kGBN;
-
-    // global -> LDS: thread t moves chunk t % 8 of tile rows t / 8 + 32 i
-    const uint32_t lc = tid & 7u, lr = tid >> 3;
-    const uint16_t* ga = a.a + (m0 + lr) * a.K + 8 * lc;
-    const uint16_t* gw = a.w + (n0 + lr) * a.K + 8 * lc;
-    const int64_t row32 = 32 * a.K;
-    u32x4 ra[4], rw[4];
-
-    // plain loads: A and W panels are shared by the tiles of an XCD through L2
-    auto load_stage = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *(const u32x4*)(ga + i * row32 + k0);
-            rw[i] = *(const u32x4*)(gw + i * row32 + k0);
-        }
-    };
-    auto store_stage = [&](int buf) {
-        uint8_t* sa = smem + buf * kGStageBytes;
-        uint8_t* sw = sa + kGBM * kGBK * 2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *(u32x4*)(sa + gemm_swz(lr + 32 * i, lc)) = ra[i];
-            *(u32x4*)(sw + gemm_swz(lr + 32 * i, lc)) = rw[i];
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-    const int64_t KT = a.K / kGBK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    // MFMA operand rows of this lane (A rows for i, W rows for j) and its
-    // 8-element half of each 16-deep step
-    const uint32_t orow = lane & 31u, ohalf = lane >> 5;
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < KT) load_stage((kt + 1) * kGBK);
-        const uint8_t* sa = smem + buf * kGStageBytes;
-        const uint8_t* sw = sa + kGBM * kGBK * 2;
-#pragma unroll
-        for (uint32_t kk = 0; kk < kGBK / 16; ++kk) {
-            const uint32_t c = 2 * kk + ohalf;
-            bf16x8 fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = *(const bf16x8*)(sa + gemm_swz(wm * 64 + 32 * i + orow, c));
-#pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(sw + gemm_swz(wn * 64 + 32 * j + orow, c));
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) store_stage(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue: x = bf16(acc) into LDS as fp32 rows of 128, then the push
-    // step on 16 rows per pass (one 16-lane DPP row per tile row)
-    float* xt = (float*)smem;   // [128][128] fp32 = 64 KB
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const uint32_t r = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * ohalf + (v & 3);
-                const uint32_t col = wn * 64 + 32 * j + orow;
-                xt[r * kGBN + col] = (float)(__bf16)acc[i][j][v];
-            }
-    __syncthreads();
-
-    const int64_t seg = m0 / a.seg_rows;        // the tile lies inside one segment
-    const bool own = seg == a.rank;
-    const uint32_t l16 = tid & 15u;
-    const bool has_comp = a.comp != nullptr;
-    for (uint32_t p = 0; p < kGBM / kRowsPerBlock; ++p) {
-        const uint32_t r = p * kRowsPerBlock + (tid >> 4);
-        const int64_t e0 = (m0 + r) * a.N + n0 + kEPL * l16;
-        float u[8];
-        {
-            const f32x4 x0 = *(const f32x4*)(xt + r * kGBN + kEPL * l16);
-            const f32x4 x1 = *(const f32x4*)(xt + r * kGBN + kEPL * l16 + 4);
-            u[0] = x0.x; u[1] = x0.y; u[2] = x0.z; u[3] = x0.w;
-            u[4] = x1.x; u[5] = x1.y; u[6] = x1.z; u[7] = x1.w;
-        }
-        if (own || a.x_all) {
-            u32x4 w;
-            w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{u[0], u[1]}), bf16x2));
-            w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{u[2], u[3]}), bf16x2));
-            w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{u[4], u[5]}), bf16x2));
-            w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{u[6], u[7]}), bf16x2));
-            st_stream((u32x4*)(a.x_out + e0), w);
-        }
-        if (own) continue;                     // uniform over the block
-        if (has_comp) {
-            const f32x4 c0 = ld_stream((const f32x4*)(a.comp + e0));
-            const f32x4 c1 = ld_stream((const f32x4*)(a.comp + e0 + 4));
-            u[0] += c0.x; u[1] += c0.y; u[2] += c0.z; u[3] += c0.w;
-            u[4] += c1.x; u[5] += c1.y; u[6] += c1.z; u[7] += c1.w;
-        }
-        float q[8];
-        const QParams prm = quantize_group<BITS, QUANT, kGBN>(u, true, lane, e0, a.codes, a.params, q);
-        if (a.err) {
-            float e[8];
-            group_error(q, prm, u, a.negate != 0, e);
-            st_stream((f32x4*)(a.err + e0), f32x4{e[0], e[1], e[2], e[3]});
-            st_stream((f32x4*)(a.err + e0 + 4), f32x4{e[4], e[5], e[6], e[7]});
-        }
-    }
-}
-
-
-// ------------------------------------------------ 256 x 256 tiles, 8 waves --
-//
-// Same computation on 256 x 256 tiles: 512 threads as 2 x 4 wavefronts of
-// 128 x 64 outputs (4 x 2 MFMA tiles, 128 accumulators per lane), so each
-// 16-deep step reads 6 operand fragments from LDS for 8 MFMAs.  Stages are
-// filled with global_load_lds_dwordx4: one instruction of a wavefront moves 8
-// rows x 128 B and lane i lands at the wave-uniform base + 16 i, i.e. row
-// i / 8, physical chunk i % 8; the lane therefore fetches the logical chunk
-// that the XOR swizzle puts there.  Two 64 KB stages, 128 KB of LDS; the
-// epilogue reuses it for the bf16 tile.
-constexpr int kG2BM = 256;
-constexpr int kG2BN = 256;
-constexpr int kG2Threads = 512;
-constexpr int kG2StageBytes = (kG2BM + kG2BN) * kGBK * 2;
-
 __device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint8_t* lds_base)
 {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -242,16 +102,16 @@ __device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint8_t* lds_
 }
 
 template <int BITS, int QUANT>
-__global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm256_push_kernel(const GemmPushArgs a)
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm256_push_kernel(const GemmPushArgs a)
 {
-    __shared__ __align__(16) uint8_t smem[2 * kG2StageBytes];   // 128 KB
+    __shared__ __align__(16) uint8_t smem[2 * kGStageBytes];   // 128 KB
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = tid >> 6;
     const uint32_t wm = wave >> 2, wn = wave & 3u;
     uint32_t tm, tn;
     gemm_tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kG2BM, n0 = (int64_t)tn * kG2BN;
+    const int64_t m0 = (int64_t)tm * kGTile, n0 = (int64_t)tn * kGTile;
 
     // this lane's share of a stage: rows wave*8 + 64 i + lane/8 (i = 0..3) of
     // A and of W, lane % 8 is the physical chunk, so it fetches the logical
@@ -262,8 +122,8 @@ __global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint16_t* gw = a.w + (n0 + wave * 8 + lrow) * a.K + 8 * lchunk;
     const int64_t row64 = 64 * a.K;
     auto issue = [&](int buf, int64_t k0) {
-        uint8_t* sa = smem + buf * kG2StageBytes;
-        uint8_t* sw = sa + kG2BM * kGBK * 2;
+        uint8_t* sa = smem + buf * kGStageBytes;
+        uint8_t* sw = sa + kGTile * kGBK * 2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t r0 = wave * 8 + 64 * i;
@@ -286,41 +146,22 @@ __global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int64_t kt = 0; kt < KT; ++kt) {
         const int buf = (int)(kt & 1);
         if (kt + 1 < KT) issue(buf ^ 1, (kt + 1) * kGBK);
-        const uint8_t* sa = smem + buf * kG2StageBytes;
-        const uint8_t* sw = sa + kG2BM * kGBK * 2;
-        // Software pipeline over the four 16-deep steps: the fragments of
-        // step kk + 2 are read while the MFMAs of step kk run, so at most 12
-        // LDS reads are in flight (the LDS counter waits on at most 15) and
-        // the MFMAs of a step wait only for that step's six reads.  The
-        // scheduling barriers keep the compiler from sinking each read to its
-        // use, which would serialize LDS latency with the MFMAs.
-        bf16x8 fa[4][4], fb[4][2];
-        auto read_step = [&](uint32_t kk) {
+        const uint8_t* sa = smem + buf * kGStageBytes;
+        const uint8_t* sw = sa + kGTile * kGBK * 2;
+#pragma unroll
+        for (uint32_t kk = 0; kk < kGBK / 16; ++kk) {
             const uint32_t c = 2 * kk + ohalf;
+            bf16x8 fa[4], fb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[kk][i] = *(const bf16x8*)(sa + gemm_swz(wm * 128 + 32 * i + orow, c));
+            for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(sa + gemm_swz(wm * 128 + 32 * i + orow, c));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[kk][j] = *(const bf16x8*)(sw + gemm_swz(wn * 64 + 32 * j + orow, c));
-        };
-        auto mfma_step = [&](uint32_t kk) {
+            for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(sw + gemm_swz(wn * 64 + 32 * j + orow, c));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
-        };
-        read_step(0);
-        read_step(1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_step(0);
-        read_step(2);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_step(1);
-        read_step(3);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_step(2);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_step(3);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the next stage has landed
         __syncthreads();
     }
@@ -336,19 +177,19 @@ __global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int v = 0; v < 16; ++v) {
                 const uint32_t r = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * ohalf + (v & 3);
                 const uint32_t col = wn * 64 + 32 * j + orow;
-                xt[r * kG2BN + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+                xt[r * kGTile + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
             }
     __syncthreads();
 
     const uint32_t l16 = tid & 15u;
-    const uint32_t gcol = ((tid >> 4) & 1u) * kGBN + kEPL * l16;
+    const uint32_t gcol = ((tid >> 4) & 1u) * kGGroup + kEPL * l16;
     const bool has_comp = a.comp != nullptr;
-    for (uint32_t p = 0; p < kG2BM / 16; ++p) {
+    for (uint32_t p = 0; p < kGTile / 16; ++p) {
         const uint32_t r = p * 16 + (tid >> 5);
         const int64_t grow = m0 + r;
         const bool own = grow / a.seg_rows == a.rank;   // uniform: segments hold whole 16-row passes
         const int64_t e0 = grow * a.N + n0 + gcol;
-        const u32x4 xw = *(const u32x4*)(xt + r * kG2BN + gcol);
+        const u32x4 xw = *(const u32x4*)(xt + r * kGTile + gcol);
         if (own || a.x_all) st_stream((u32x4*)(a.x_out + e0), xw);
         if (own) continue;
         float u[8];
@@ -360,7 +201,7 @@ __global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2
             u[4] += c1.x; u[5] += c1.y; u[6] += c1.z; u[7] += c1.w;
         }
         float q[8];
-        const QParams prm = quantize_group<BITS, QUANT, kGBN>(u, true, lane, e0, a.codes, a.params, q);
+        const QParams prm = quantize_group<BITS, QUANT, kGGroup>(u, true, lane, e0, a.codes, a.params, q);
         if (a.err) {
             float e[8];
             group_error(q, prm, u, a.negate != 0, e);
@@ -369,5 +210,6 @@ __global__ __launch_bounds__(kG2Threads) __attribute__((amdgpu_waves_per_eu(2, 2
         }
     }
 }
+
 
 }  // namespace echo
