@@ -327,7 +327,7 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
 {
     if (P < 1 || P > ECHO_MAX_P) return ECHO_EINVAL;
     if (bits != 4 && bits != 8) return ECHO_EUNSUP;
-    if (group != echo::kGGroup) return ECHO_EUNSUP;   // one group = 128 columns of a row
+    if (group != 128 && group != 256) return ECHO_EUNSUP;   // one group = 128 or 256 columns of a row
     if (M < 0 || N < 0 || K < 0) return ECHO_ESHAPE;
     if (N % echo::kGTile || M % echo::kGTile || M % P || (M / P) % 16) return ECHO_ESHAPE;
     if (M != 0 && N != 0 && (K == 0 || K % echo::kGBK)) return ECHO_ESHAPE;
@@ -348,7 +348,13 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
     const int q = quant_of(flags);
     g.tiles_m = (uint32_t)(M / echo::kGTile); g.tiles_n = (uint32_t)(N / echo::kGTile);
     const dim3 grid(g.tiles_m * g.tiles_n);
-#define ECHO_GEMM_GO(B, Q) hipLaunchKernelGGL((echo::gemm256_push_kernel<B, Q>), grid, dim3(echo::kGThreads), 0, st, g)
+#define ECHO_GEMM_GO(B, Q)                                                                                  \
+    do {                                                                                                    \
+        if (group == 128)                                                                                   \
+            hipLaunchKernelGGL((echo::gemm256_push_kernel<B, Q, 128>), grid, dim3(echo::kGThreads), 0, st, g); \
+        else                                                                                                \
+            hipLaunchKernelGGL((echo::gemm256_push_kernel<B, Q, 256>), grid, dim3(echo::kGThreads), 0, st, g); \
+    } while (0)
     if (bits == 4) {
         if (q == echo::kZeroAware) ECHO_GEMM_GO(4, echo::kZeroAware);
         else if (q == echo::kNaive) ECHO_GEMM_GO(4, echo::kNaive);

@@ -37,7 +37,7 @@
 namespace echo {
 
 constexpr int kGTile = 256;                            // tile rows = tile columns
-constexpr int kGGroup = 128;                           // columns of one quantization group
+constexpr int kGHalf = 128;                            // columns of one 16-lane row in the epilogue
 constexpr int kGBK = 64;                               // K per stage
 constexpr int kGThreads = 512;                         // 8 wavefronts
 constexpr int kGChunks = kGBK / 8;                     // 16-byte chunks per stage row
@@ -101,7 +101,7 @@ __device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint8_t* lds_
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-template <int BITS, int QUANT>
+template <int BITS, int QUANT, int GROUP>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm256_push_kernel(const GemmPushArgs a)
 {
     __shared__ __align__(16) uint8_t smem[2 * kGStageBytes];   // 128 KB
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     __syncthreads();
 
     const uint32_t l16 = tid & 15u;
-    const uint32_t gcol = ((tid >> 4) & 1u) * kGGroup + kEPL * l16;
+    const uint32_t gcol = ((tid >> 4) & 1u) * kGHalf + kEPL * l16;
     const bool has_comp = a.comp != nullptr;
     for (uint32_t p = 0; p < kGTile / 16; ++p) {
         const uint32_t r = p * 16 + (tid >> 5);
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             u[4] += c1.x; u[5] += c1.y; u[6] += c1.z; u[7] += c1.w;
         }
         float q[8];
-        const QParams prm = quantize_group<BITS, QUANT, kGGroup>(u, true, lane, e0, a.codes, a.params, q);
+        const QParams prm = quantize_group<BITS, QUANT, GROUP>(u, true, lane, e0, a.codes, a.params, q);
         if (a.err) {
             float e[8];
             group_error(q, prm, u, a.negate != 0, e);

@@ -206,7 +206,7 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  * and then does exactly what echo_quantize_ef(x, comp, M*N, P, rank, 0,
  * M*N/P, bits, group, codes, params, err, flags) does, without writing x for
  * the pushed segments: the message is x in row-major order, segment s is
- * rows [s*M/P, (s+1)*M/P), one group is 128 consecutive columns of a row.
+ * rows [s*M/P, (s+1)*M/P), one group is `group` consecutive columns of a row.
  * The rank's own segment of x is written to x_out (bf16), for the owner
  * reduce; with ECHO_X_ALL, x_out receives every segment.  The fp32 sum order
  * is the kernel's own (K in steps of 16, MFMA accumulation), so x matches a
@@ -221,7 +221,7 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  *                         alias comp or be NULL)
  *   x_out  (device, out)  bfloat16 bits [M*N]; rows of segment `rank` (all
  *                         rows with ECHO_X_ALL) are written, others untouched
- * Constraints: group == 128 (ECHO_EUNSUP otherwise); M and N multiples of
+ * Constraints: group 128 or 256 (ECHO_EUNSUP otherwise); M and N multiples of
  * 256, K a positive multiple of 64, M a multiple of P with M/P a multiple of
  * 16, M*N <= 2^34 (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those
  * of echo_quantize_ef and ECHO_X_ALL.

@@ -199,7 +199,7 @@ def matmul_bf16(a, w) -> np.ndarray:
     return f32_to_bf16_bits((a64 @ w64.T).astype(np.float32)).reshape(-1)
 
 
-def gemm_quantize_ef(a, w, comp, P, rank, bits, codes, params, err, x_out, flags=0, x=None):
+def gemm_quantize_ef(a, w, comp, P, rank, bits, codes, params, err, x_out, flags=0, x=None, group=128):
     """The fused matmul + entry pass as its two steps: x = matmul_bf16(A, W)
     (or the given x), then quantize_ef over the whole message (segment s =
     rows [s*M/P, (s+1)*M/P)); the rank's own rows of x go to x_out (every row
@@ -208,7 +208,7 @@ def gemm_quantize_ef(a, w, comp, P, rank, bits, codes, params, err, x_out, flags
     n = M * N
     if x is None:
         x = matmul_bf16(a, w)
-    quantize_ef(x, comp, n, P, rank, 0, n // P, bits, 128, codes, params, err, flags & ~X_ALL)
+    quantize_ef(x, comp, n, P, rank, 0, n // P, bits, group, codes, params, err, flags & ~X_ALL)
     if flags & X_ALL:
         x_out[:] = x
     else:

@@ -75,7 +75,7 @@ def test_gemm_quantize_ef_argument_checks():
                            kw.get("rank", 0), kw.get("bits", 4), kw.get("group", 128), kw.get("codes", FAKE),
                            kw.get("params", FAKE), kw.get("err", None), kw.get("x_out", FAKE),
                            kw.get("flags", 0), stream=0)
-    assert g(bits=2) == echo.EUNSUP and g(group=256) == echo.EUNSUP
+    assert g(bits=2) == echo.EUNSUP and g(group=64) == echo.EUNSUP
     assert g(P=0) == echo.EINVAL and g(P=9) == echo.EINVAL and g(rank=4) == echo.EINVAL
     assert g(N=N + 128) == echo.ESHAPE                # N not a multiple of 256
     assert g(K=K + 32) == echo.ESHAPE and g(K=0) == echo.ESHAPE

@@ -41,12 +41,12 @@ def operands(rank, M, N, K, kind, site=0):
     return inputs.as_numpy_u16(a).reshape(M, K), inputs.as_numpy_u16(w).reshape(N, K)
 
 
-def run_gpu(echo, a, w, comp, P, rank, bits, flags, with_err, err_in_place):
+def run_gpu(echo, a, w, comp, P, rank, bits, flags, with_err, err_in_place, group=128):
     M, K = a.shape
     N = w.shape[0]
     n = M * N
     cd = dev_u8(np.zeros(oracle.code_bytes(n, bits), np.uint8))
-    pd = params_dev(n // 128, 0)
+    pd = params_dev(n // group, 0)
     comp_d = dev_f32(comp) if comp is not None else None
     if err_in_place:
         err_d = comp_d
@@ -55,17 +55,17 @@ def run_gpu(echo, a, w, comp, P, rank, bits, flags, with_err, err_in_place):
     else:
         err_d = None
     x_d = dev_u16(np.full(n, SENT, np.uint16))
-    echo.echo_gemm_quantize_ef(dev_u16(a), dev_u16(w), M, N, K, comp_d, P, rank, bits, 128, cd, pd, err_d,
+    echo.echo_gemm_quantize_ef(dev_u16(a), dev_u16(w), M, N, K, comp_d, P, rank, bits, group, cd, pd, err_d,
                                x_d, flags)
     torch.cuda.synchronize()
     return (host_u8(cd), host_u16(pd), host_f32(err_d) if err_d is not None else None, host_u16(x_d))
 
 
-def run_oracle(a, w, comp, P, rank, bits, flags, with_err, err_in_place, x=None):
+def run_oracle(a, w, comp, P, rank, bits, flags, with_err, err_in_place, x=None, group=128):
     M, N = a.shape[0], w.shape[0]
     n = M * N
     codes = np.zeros(oracle.code_bytes(n, bits), np.uint8)
-    params = np.zeros(2 * n // 128, np.uint16)
+    params = np.zeros(2 * n // group, np.uint16)
     comp_h = comp.copy() if comp is not None else None
     if err_in_place:
         err = comp_h
@@ -74,26 +74,28 @@ def run_oracle(a, w, comp, P, rank, bits, flags, with_err, err_in_place, x=None)
     else:
         err = None
     x_out = np.full(n, SENT, np.uint16)
-    x = oracle.gemm_quantize_ef(a, w, comp_h, P, rank, bits, codes, params, err, x_out, flags, x=x)
+    x = oracle.gemm_quantize_ef(a, w, comp_h, P, rank, bits, codes, params, err, x_out, flags, x=x, group=group)
     return codes, params, err, x_out, x
 
 
 INT_CASES = [
-    # M, N, K, P, bits, quant, mode
-    (512, 256, 128, 4, 4, "zero_aware", "negated_in_place"),
-    (512, 512, 128, 4, 8, "zero_aware", "err"),
-    (512, 768, 192, 4, 4, "naive", "comp_only"),
-    (256, 256, 64, 2, 4, "symmetric", "negated_in_place"),
-    (1024, 256, 320, 8, 8, "naive", "negated_in_place"),
-    (1024, 512, 128, 8, 4, "zero_aware", "plain"),
-    (512, 256, 128, 8, 4, "zero_aware", "negated_in_place"),   # 64-row segments: 4 per tile
-    (768, 256, 64, 3, 4, "symmetric", "err"),
-    (256, 256, 256, 1, 4, "zero_aware", "err"),
+    # M, N, K, P, bits, quant, mode, group
+    (512, 256, 128, 4, 4, "zero_aware", "negated_in_place", 128),
+    (512, 512, 128, 4, 8, "zero_aware", "err", 128),
+    (512, 768, 192, 4, 4, "naive", "comp_only", 128),
+    (256, 256, 64, 2, 4, "symmetric", "negated_in_place", 128),
+    (1024, 256, 320, 8, 8, "naive", "negated_in_place", 128),
+    (1024, 512, 128, 8, 4, "zero_aware", "plain", 128),
+    (512, 256, 128, 8, 4, "zero_aware", "negated_in_place", 128),   # 64-row segments: 4 per tile
+    (768, 256, 64, 3, 4, "symmetric", "err", 128),
+    (256, 256, 256, 1, 4, "zero_aware", "err", 128),
+    (512, 512, 128, 4, 4, "zero_aware", "negated_in_place", 256),
+    (512, 256, 192, 2, 8, "naive", "err", 256),
 ]
 
 
-@pytest.mark.parametrize("M,N,K,P,bits,quant,mode", INT_CASES)
-def test_fused_gemm_push_exact_operands(echo, M, N, K, P, bits, quant, mode):
+@pytest.mark.parametrize("M,N,K,P,bits,quant,mode,group", INT_CASES)
+def test_fused_gemm_push_exact_operands(echo, M, N, K, P, bits, quant, mode, group):
     flags = echo.QUANTS[quant] | (echo.ERR_NEGATED if mode == "negated_in_place" else 0)
     comp = None
     if mode in ("negated_in_place", "err", "comp_only"):
@@ -102,10 +104,10 @@ def test_fused_gemm_push_exact_operands(echo, M, N, K, P, bits, quant, mode):
     in_place = mode == "negated_in_place"
     for rank in sorted({0, P - 1, P // 2}):
         for x_all in (0, echo.X_ALL):
-            say("gemm exact", M, N, K, P, bits, quant, mode, rank, x_all)
+            say("gemm exact", M, N, K, P, bits, quant, mode, group, rank, x_all)
             a, w = operands(rank, M, N, K, "int")
-            got = run_gpu(echo, a, w, comp, P, rank, bits, flags | x_all, with_err, in_place)
-            want = run_oracle(a, w, comp, P, rank, bits, flags | x_all, with_err, in_place)
+            got = run_gpu(echo, a, w, comp, P, rank, bits, flags | x_all, with_err, in_place, group)
+            want = run_oracle(a, w, comp, P, rank, bits, flags | x_all, with_err, in_place, group=group)
             assert_bits_equal(got[3], want[3], "x_out")
             assert_bits_equal(got[0], want[0], "codes")
             assert_bits_equal(got[1], want[1], "params")
