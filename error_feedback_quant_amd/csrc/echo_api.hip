@@ -335,9 +335,11 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
     if (rank < 0 || rank >= P) return ECHO_EINVAL;
     if ((flags & ~(kKnownFlags | ECHO_X_ALL)) || quant_of(flags) < 0) return ECHO_EINVAL;
     if (M == 0 || N == 0) return ECHO_OK;
-    if (!a_bf16 || !w_bf16 || !codes || !params || !x_out) return ECHO_EINVAL;
-    if (!aligned16(a_bf16) || !aligned16(w_bf16) || !aligned16(codes) || !aligned16(params) ||
-        !aligned16(x_out) || (comp && !aligned16(comp)) || (err && !aligned16(err)))
+    // with P == 1 nothing is pushed and codes / params may be NULL
+    if (!a_bf16 || !w_bf16 || !x_out || (P > 1 && (!codes || !params))) return ECHO_EINVAL;
+    if (!aligned16(a_bf16) || !aligned16(w_bf16) || (codes && !aligned16(codes)) ||
+        (params && !aligned16(params)) || !aligned16(x_out) || (comp && !aligned16(comp)) ||
+        (err && !aligned16(err)))
         return ECHO_EALIGN;
     echo::GemmPushArgs g;
     g.a = a_bf16; g.w = w_bf16; g.comp = comp; g.codes = codes; g.params = (uint32_t*)params;

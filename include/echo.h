@@ -225,7 +225,8 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  * 256, K a positive multiple of 64, M a multiple of P with M/P a multiple of
  * 16, M*N <= 2^34 (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those
  * of echo_quantize_ef and ECHO_X_ALL.
- * Pointers as for echo_quantize_ef, plus a_bf16, w_bf16 and x_out required.
+ * Pointers as for echo_quantize_ef (codes and params may be NULL when P == 1,
+ * as nothing is pushed), plus a_bf16, w_bf16 and x_out required.
  */
 int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,
                           int64_t K, const float* comp, int P, int rank, int bits, int group,
