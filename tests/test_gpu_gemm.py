@@ -152,3 +152,15 @@ def test_fused_gemm_push_llama_down_projection(echo):
     M, N, K, P = shp["tokens"], shp["hidden"], shp["k"], shp["P"]
     say("gemm llama down-proj", M, N, K, P)
     check_normal(echo, M, N, K, P, 1, 4, echo.ERR_NEGATED)
+
+
+def test_single_rank_writes_x_and_needs_no_code_buffers(echo):
+    """P = 1: every row is the rank's own, nothing is pushed, so the call is
+    the matmul alone and takes NULL codes and parameters."""
+    M, N, K = 256, 512, 192
+    a, w = operands(0, M, N, K, "int")
+    x_d = dev_u16(np.full(M * N, SENT, np.uint16))
+    say("gemm P=1 no codes", M, N, K)
+    echo.echo_gemm_quantize_ef(dev_u16(a), dev_u16(w), M, N, K, None, 1, 0, 4, 128, None, None, None, x_d, 0)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(x_d), oracle.matmul_bf16(a, w), "x_out")
