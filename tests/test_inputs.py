@@ -36,3 +36,22 @@ def test_single_outliers_and_chain_shapes():
     z = f32(inputs.chain8(0, 0, tokens=64, hidden=1024))
     frac_small = (np.abs(z) < 1e-3).mean()
     assert 0.29 < frac_small < 0.33                          # 30 % near-zero mass (+1.6 % from N(0,0.05))
+
+
+def test_tp_operands_recipes():
+    a, w = inputs.tp_operands(0, 64, 32, 256, "int")
+    A, W = f32(a.reshape(-1)), f32(w.reshape(-1))
+    assert a.shape == (64, 256) and w.shape == (32, 256)
+    assert np.array_equal(A, np.round(A)) and A.min() >= -4 and A.max() <= 4
+    assert np.array_equal(W, np.round(W)) and W.min() >= -3 and W.max() <= 3
+    # every product and partial sum of a row is an integer below 2^24: exact in fp32
+    assert 256 * 4 * 3 < 2 ** 24
+    a, w = inputs.tp_operands(1, 256, 128, 1024, "normal")
+    A, W = f32(a.reshape(-1)), f32(w.reshape(-1))
+    assert abs(A.std() - 1.0) < 0.02 and abs(W.std() * math.sqrt(1024) - 1.0) < 0.03
+    # the partial sums of a random-init layer have unit scale
+    x = (A.reshape(256, 1024).astype(np.float64) @ W.reshape(128, 1024).astype(np.float64).T)
+    assert 0.9 < x.std() < 1.1
+    # seeded: the same rank gives the same draw, another rank a different one
+    assert torch.equal(inputs.tp_operands(1, 8, 8, 64)[0], inputs.tp_operands(1, 8, 8, 64)[0])
+    assert not torch.equal(inputs.tp_operands(1, 8, 8, 64)[0], inputs.tp_operands(2, 8, 8, 64)[0])
