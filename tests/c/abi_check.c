@@ -46,6 +46,18 @@ int main(void)
     expect("compensate alpha", echo_compensate((const float*)fake, (float*)fake, NULL, 1024, 0.5f, 0.0f, NULL),
            ECHO_EINVAL);
     expect("workspace size", (int)(echo_allreduce_sim_workspace_bytes(4, 4096, 4, 128) == 5 * (2048 + 256)), 1);
+    expect("gemm N % 256", echo_gemm_quantize_ef(x, x, 512, 384, 128, NULL, 4, 0, 4, 128, codes, params, NULL,
+                                                 (uint16_t*)fake, 0, NULL),
+           ECHO_ESHAPE);
+    expect("gemm group 64", echo_gemm_quantize_ef(x, x, 512, 256, 128, NULL, 4, 0, 4, 64, codes, params, NULL,
+                                                  (uint16_t*)fake, 0, NULL),
+           ECHO_EUNSUP);
+    expect("gemm x_out NULL", echo_gemm_quantize_ef(x, x, 512, 256, 128, NULL, 4, 0, 4, 128, codes, params, NULL,
+                                                    NULL, ECHO_X_ALL, NULL),
+           ECHO_EINVAL);
+    expect("gemm empty", echo_gemm_quantize_ef(x, x, 0, 256, 128, NULL, 4, 0, 4, 128, codes, params, NULL,
+                                               (uint16_t*)fake, 0, NULL),
+           ECHO_OK);
 
     echo_sim_args a;
     memset(&a, 0, sizeof a);
