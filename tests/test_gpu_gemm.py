@@ -164,3 +164,42 @@ def test_single_rank_writes_x_and_needs_no_code_buffers(echo):
     echo.echo_gemm_quantize_ef(dev_u16(a), dev_u16(w), M, N, K, None, 1, 0, 4, 128, None, None, None, x_d, 0)
     torch.cuda.synchronize()
     assert_bits_equal(host_u16(x_d), oracle.matmul_bf16(a, w), "x_out")
+
+
+@pytest.mark.parametrize("P,M", [(4, 512), (8, 256)])
+def test_fused_gemm_feeds_the_allreduce(echo, P, M):
+    """End to end through the C ABI: every rank's fused matmul + push, then each
+    owner's reduce (reading the own rows the fused call wrote) and every
+    rank's tail, two calls in a row with classic feedback carried in place.
+    Against the oracle's whole call on the same partial sums x_r =
+    bf16(A_r W_r^T): outputs and compensations bit for bit (integer operands,
+    so x_r is exact; P = 8 with M = 256 has 32-row segments, eight per tile)."""
+    N, K, bits, G = 256, 128, 4, 128
+    n = M * N
+    S = n // P
+    rng = np.random.default_rng(300 + P)
+    comps_h = [(rng.standard_normal(n) * 0.5).astype(np.float32) for _ in range(P)]
+    comps_d = [dev_f32(c) for c in comps_h]
+    ws_codes = [dev_u8(np.zeros(n // 2, np.uint8)) for _ in range(P)]
+    ws_params = [params_dev(n // G, 0) for _ in range(P)]
+    x_d = [dev_u16(np.full(n, SENT, np.uint16)) for _ in range(P)]
+    sc = dev_u8(np.zeros(n // 2, np.uint8))
+    sp = params_dev(n // G, 0)
+    for call in range(2):
+        ops = [operands(r, M, N, K, "int", site=call) for r in range(P)]
+        xs = [oracle.matmul_bf16(a, w) for a, w in ops]
+        say("gemm -> allreduce", P, M, call)
+        for r, (a, w) in enumerate(ops):
+            echo.echo_gemm_quantize_ef(dev_u16(a), dev_u16(w), M, N, K, comps_d[r], P, r, bits, G, ws_codes[r],
+                                       ws_params[r], comps_d[r], x_d[r], echo.ERR_NEGATED)
+        for o in range(P):
+            echo.echo_reduce_segment(x_d[o], comps_d[o], ws_codes, ws_params, P, o, n, 0, S, bits, G, sc, sp,
+                                     comps_d[o], echo.ERR_NEGATED)
+        outs_d = [dev_f32(np.zeros(n, np.float32)) for _ in range(P)]
+        for r in range(P):
+            echo.echo_gather_dequant(sc, sp, n, 0, S, P, bits, G, outs_d[r], echo.OUT_F32)
+        torch.cuda.synchronize()
+        want, _, _ = oracle.allreduce(xs, bits=bits, group=G, ef=True, comps=comps_h, out_dtype=oracle.OUT_F32)
+        for r in range(P):
+            assert_bits_equal(host_f32(outs_d[r]), want[r], f"output of rank {r}, call {call}")
+            assert_bits_equal(host_f32(comps_d[r]), comps_h[r], f"compensation of rank {r}, call {call}")
