@@ -330,7 +330,7 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
     if (group != 128 && group != 256) return ECHO_EUNSUP;   // one group = 128 or 256 columns of a row
     if (M < 0 || N < 0 || K < 0) return ECHO_ESHAPE;
     if (N % echo::kGTile || M % echo::kGTile || M % P || (M / P) % 16) return ECHO_ESHAPE;
-    if (M != 0 && N != 0 && (K == 0 || K % echo::kGBK)) return ECHO_ESHAPE;
+    if (M != 0 && N != 0 && (K == 0 || K % echo::kGBK || K > echo::kGMaxK)) return ECHO_ESHAPE;
     if (N != 0 && M > kMaxN / N) return ECHO_ESHAPE;
     if (rank < 0 || rank >= P) return ECHO_EINVAL;
     if ((flags & ~(kKnownFlags | ECHO_X_ALL)) || quant_of(flags) < 0) return ECHO_EINVAL;

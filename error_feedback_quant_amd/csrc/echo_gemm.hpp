@@ -23,13 +23,17 @@
 // Main loop: 512 threads per 256 x 256 tile as 2 x 4 wavefronts of 128 x 64
 // outputs (4 x 2 tiles of v_mfma_f32_32x32x16_bf16, 128 accumulators per
 // lane), K in stages of 64, so each 16-deep step reads 6 operand fragments
-// from LDS for 8 MFMAs.  Stages are filled with global_load_lds_dwordx4: one
-// instruction of a wavefront moves 8 rows x 128 B and lane i lands at the
-// wave-uniform base + 16 i (row i / 8, physical chunk i % 8), so the lane
-// fetches the logical chunk that the XOR swizzle puts there.  Two 64 KB
-// stages, 128 KB of LDS; the epilogue reuses it for the bf16 tile.  The tile
-// order is XCD-aware: the 8 XCDs each take a compact block of tiles, so that
-// the A and W panels a tile needs are shared in that XCD's L2.
+// from LDS for 8 MFMAs.  Stages are filled with buffer_load_dwordx4 ... lds
+// through a buffer resource over the tile's A (or W) panel: one instruction
+// of a wavefront moves 8 rows x 128 B and lane i lands at the wave-uniform
+// LDS base + 16 i (row i / 8, physical chunk i % 8), so the lane fetches the
+// logical chunk that the XOR swizzle puts there.  (The global_load_lds form
+// of the same load, a FLAT-encoded instruction, slowed the MFMA loop by
+// about 13 %, and the compiler counts it as an LDS event, which turns every
+// LDS wait in the loop into a wait for zero.)  Two 64 KB stages, 128 KB of
+// LDS; the epilogue reuses it for the bf16 tile.  The tile order is
+// XCD-aware: the 8 XCDs each take a compact block of tiles, so that the A and
+// W panels a tile needs are shared in that XCD's L2.
 #pragma once
 
 #include "echo_kernels.hpp"
@@ -43,6 +47,7 @@ constexpr int kGThreads = 512;                         // 8 wavefronts
 constexpr int kGChunks = kGBK / 8;                     // 16-byte chunks per stage row
 constexpr int kGStageBytes = 2 * kGTile * kGBK * 2;    // A + W, one stage (64 KB)
 constexpr int kGXcds = 8;
+constexpr int64_t kGMaxK = (int64_t(1) << 22) - kGBK;  // a 256-row panel stays below 2^31 bytes
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -95,10 +100,18 @@ __device__ __forceinline__ void gemm_tile_of(uint32_t b, uint32_t tm_n, uint32_t
     tn = in / rows;
 }
 
-__device__ __forceinline__ void gemm_load_lds16(const uint16_t* g, uint8_t* lds_base)
+// buffer resource over `rows` rows of a [.][K] bf16 matrix starting at p:
+// stride 0, so the record count is in bytes; dword 3 selects 32-bit raw
+// data.  A lane's offset is below rows*K*2 < 2^31 (K < 2^22 is checked on
+// the host), and an offset past the record count would read 0, not fault.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_panel_rsrc(const uint16_t* p, int64_t rows, int64_t K)
 {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(rows * K * 2), 0x00020000);
+}
+
+__device__ __forceinline__ void gemm_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint8_t* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_off, 0, 0, 0);
 }
 
 template <int BITS, int QUANT, int GROUP>
@@ -118,17 +131,19 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // chunk (lane % 8) ^ key(row); key(row) is the same for every i
     const uint32_t lrow = lane >> 3;
     const uint32_t lchunk = (lane & 7u) ^ gemm_swz_key(wave * 8 + lrow);
-    const uint16_t* ga = a.a + (m0 + wave * 8 + lrow) * a.K + 8 * lchunk;
-    const uint16_t* gw = a.w + (n0 + wave * 8 + lrow) * a.K + 8 * lchunk;
-    const int64_t row64 = 64 * a.K;
+    const __amdgpu_buffer_rsrc_t ra = gemm_panel_rsrc(a.a + m0 * a.K, kGTile, a.K);
+    const __amdgpu_buffer_rsrc_t rw = gemm_panel_rsrc(a.w + n0 * a.K, kGTile, a.K);
+    const uint32_t lane_off = (uint32_t)(((wave * 8 + lrow) * a.K + 8 * lchunk) * 2);
+    const uint32_t row64 = (uint32_t)(64 * a.K * 2);
     auto issue = [&](int buf, int64_t k0) {
         uint8_t* sa = smem + buf * kGStageBytes;
         uint8_t* sw = sa + kGTile * kGBK * 2;
+        const uint32_t off = lane_off + (uint32_t)(k0 * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t r0 = wave * 8 + 64 * i;
-            gemm_load_lds16(ga + i * row64 + k0, sa + r0 * (kGChunks * 16));
-            gemm_load_lds16(gw + i * row64 + k0, sw + r0 * (kGChunks * 16));
+            gemm_load_lds16(ra, off + i * row64, sa + r0 * (kGChunks * 16));
+            gemm_load_lds16(rw, off + i * row64, sw + r0 * (kGChunks * 16));
         }
     };
 

@@ -222,8 +222,8 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  *   x_out  (device, out)  bfloat16 bits [M*N]; rows of segment `rank` (all
  *                         rows with ECHO_X_ALL) are written, others untouched
  * Constraints: group 128 or 256 (ECHO_EUNSUP otherwise); M and N multiples of
- * 256, K a positive multiple of 64, M a multiple of P with M/P a multiple of
- * 16, M*N <= 2^34 (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those
+ * 256, K a positive multiple of 64 below 2^22, M a multiple of P with
+ * M/P a multiple of 16, M*N <= 2^34 (ECHO_ESHAPE); M or N of 0 enqueues nothing.  Flags: those
  * of echo_quantize_ef and ECHO_X_ALL.
  * Pointers as for echo_quantize_ef (codes and params may be NULL when P == 1,
  * as nothing is pushed), plus a_bf16, w_bf16 and x_out required.

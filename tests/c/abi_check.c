@@ -55,6 +55,9 @@ int main(void)
     expect("gemm x_out NULL", echo_gemm_quantize_ef(x, x, 512, 256, 128, NULL, 4, 0, 4, 128, codes, params, NULL,
                                                     NULL, ECHO_X_ALL, NULL),
            ECHO_EINVAL);
+    expect("gemm K = 2^22", echo_gemm_quantize_ef(x, x, 512, 256, (int64_t)1 << 22, NULL, 4, 0, 4, 128, codes,
+                                                  params, NULL, (uint16_t*)fake, 0, NULL),
+           ECHO_ESHAPE);
     expect("gemm empty", echo_gemm_quantize_ef(x, x, 0, 256, 128, NULL, 4, 0, 4, 128, codes, params, NULL,
                                                (uint16_t*)fake, 0, NULL),
            ECHO_OK);

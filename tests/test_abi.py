@@ -83,6 +83,7 @@ def test_gemm_quantize_ef_argument_checks():
     assert g(M=256, P=3) == echo.ESHAPE               # M not a multiple of P
     assert g(M=-128) == echo.ESHAPE
     assert g(M=1 << 22, N=1 << 13) == echo.ESHAPE     # M * N beyond 2^34
+    assert g(K=1 << 22) == echo.ESHAPE                # a 256-row operand panel would reach 2^31 bytes
     assert g(a=None) == echo.EINVAL and g(w=None) == echo.EINVAL and g(x_out=None) == echo.EINVAL
     assert g(codes=None) == echo.EINVAL
     assert g(a=FAKE + 2) == echo.EALIGN and g(err=FAKE + 4) == echo.EALIGN
