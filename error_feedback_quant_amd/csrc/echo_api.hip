@@ -4,8 +4,8 @@
 // The calls follow the problem statement of "Echo: Error-Compensated 4-Bit
 // Tensor-Parallel Communication for LLM Training and Inference" (arXiv
 // 2610.14277): Fig. 2(a) (push, owner reduce, quantized all-gather, decode),
-// Fig. 2(b) (tiles staggered across push, reduce, gather and tail, with
-// events ordering the work inside one GPU), and the PhantomByte article's
+// Fig. 2(b) (the push, reduce, gather and tail of successive tiles overlap,
+// with events ordering the work inside one GPU), and the PhantomByte article's
 // "The cancellation rule" (compensator fused into the entry pass, update run
 // beside the next matmul).  Semantics, layouts and error behaviour are
 // specified in include/echo.h.

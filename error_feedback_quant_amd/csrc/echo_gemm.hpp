@@ -3,10 +3,10 @@
 //
 // Method: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for LLM
 // Training and Inference" (arXiv 2610.14277), paper card Fig. 2(a) (each rank
-// quantizes its partial sums for the segments it does not own); PhantomByte
-// article on Echo, "The cancellation rule" (the compensator is folded into
-// the entry pass of the all-reduce, next to the matmul that produces the
-// partial sums, without changing the computed values).
+// quantizes its partial sums for the segments owned by others); PhantomByte
+// article on Echo, "The cancellation rule" (adding the compensation moves
+// into the all-reduce's first pass, beside the matmul whose partial sums it
+// sends, and the results stay the same).
 //
 // One launch computes one rank's partial sums X = A W^T (A: M x K, W: N x K,
 // both bf16 with K contiguous, fp32 accumulation), rounds them to bf16 and,

@@ -11,10 +11,11 @@
  * The problem: P tensor-parallel ranks each hold a partial sum x_r of n
  * bfloat16 values; the all-reduce returns sum_r x_r to every rank.  Echo
  * splits the message into P equal contiguous segments, segment s owned by
- * rank s.  Each rank adds its compensation, quantizes the P-1 segments it
- * does not own and pushes the codes to their owners; each owner dequantizes
- * them, adds its own unquantized segment in fp32 and quantizes the sum once;
- * every rank decodes that same code.  The errors the sum reveals feed a
+ * rank s.  Each rank adds its compensation, quantizes the P-1 segments that
+ * belong to other ranks and sends those codes to the segments' owners; an
+ * owner decodes the P-1 copies it received, adds its own copy (never
+ * quantized) in fp32 and quantizes the total a single time; every rank
+ * decodes that same code.  The errors the sum reveals feed a
  * compensator whose output is added at the next call.
  *
  * Here the P ranks are P sets of buffers on one GPU: "push" and "gather"
@@ -131,10 +132,10 @@ int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P
 
 /*
  * echo_reduce_segment — the owner's high-precision sum and single
- * requantization.  Paper card Fig. 2(a) (the owner dequantizes the received
- * codes and adds its own unquantized segment in high precision; the reduced
- * segment is quantized once for the all-gather), Fig. 4, abstract (the sum
- * reveals each injected error).
+ * requantization.  Paper card Fig. 2(a) (decode of the peers' codes, the
+ * owner's own copy added without quantization, one quantization of the total
+ * before the all-gather), Fig. 4, abstract (the sum reveals each injected
+ * error).
  *
  * For every group of segment `owner` inside the tile:
  *   t_j = float(own_x) + own_comp       when j == owner (no quantization)
@@ -174,9 +175,9 @@ int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params,
 
 /*
  * echo_compensate — the two-timescale compensator update, elementwise.
- * Paper card abstract (revealed errors are fed back into later calls, so old
- * errors cancel); article "The cancellation rule" (a two-timescale
- * compensator; the update runs beside the next matrix multiplication).  The
+ * Paper card abstract (a revealed error is returned in a later call, which
+ * cancels it); article "The cancellation rule" (a two-timescale compensator,
+ * updated off the critical path while the next matmul runs).  The
  * pages give no equation; the reading is an error debt with a fast fraction
  * alpha returned at the next call and a slow memory M released at rate beta:
  *   comp_next = -(alpha*e + beta*M)
@@ -196,7 +197,7 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
 /*
  * echo_gemm_quantize_ef — one rank's row-parallel matmul with the entry pass
  * and push quantization fused into its epilogue.  Paper card Fig. 2(a) (each
- * rank quantizes its partial sums for the segments it does not own);
+ * rank quantizes its partial sums for the segments owned by other ranks);
  * article "The cancellation rule" (the compensator is folded into the entry
  * pass, beside the matmul, without changing the computed values).
  *
@@ -236,9 +237,9 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
 /*
  * echo_allreduce_sim — one whole call for P simulated ranks: push, owner
  * reduce, gather, tail decode and (if on) the compensator update, with each
- * segment split into `tiles` tiles staggered across streams.  Paper card
- * Fig. 2(b) (tiles staggered across push, reduce, gather and tail; events
- * order the work inside a GPU).
+ * segment split into `tiles` tiles whose stages overlap on several streams.
+ * Paper card Fig. 2(b) (the stages of successive tiles overlap in time;
+ * events order the work inside a GPU).
  *
  * Stage k of every tile runs on streams[k % nstreams] (push 0, reduce 1,
  * tail 2, compensator 3); events order tile t's reduce after its pushes and

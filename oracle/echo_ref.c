@@ -27,7 +27,8 @@
  *     named in Fig. 4 but not printed) is the min/max affine quantizer whose
  *     range is widened to contain 0, with an integer zero point so that 0 is
  *     a grid point; its scale and zero point are stored as IEEE binary16
- *     ([Blog], "4-bit integers with half-precision parameters per group");
+ *     ([Blog] "The cancellation rule": the codes travel as 4-bit integers
+ *     and each group's parameters at half precision);
  *   - codes are unsigned in [0, 2^b-1]; for b = 4 two codes share a byte,
  *     the even element in the low nibble;
  *   - segment s (P equal contiguous segments) is owned by rank s;
@@ -352,7 +353,7 @@ static int check_shape(int64_t n, int P, int64_t tile_begin, int64_t tile_len,
 
 /* ------------------------------------------------------------------------ */
 /* O2: entry pass + push quantize, for one rank.                             */
-/* [EchoCard] Fig. 2(a) (each rank quantizes the segments it does not own);  */
+/* [EchoCard] Fig. 2(a) (a rank quantizes only segments other ranks own);   */
 /* Fig. 4 (three quantized copies, own copy kept); [Blog] "The cancellation  */
 /* rule" (compensation fused into the entry pass).                           */
 /* For every segment s != rank and every group of the tile [tile_begin,      */
@@ -406,10 +407,11 @@ int echo_ref_quantize_ef(const uint16_t* x, const float* comp, int64_t n, int P,
 
 /* ------------------------------------------------------------------------ */
 /* O3: owner reduce, for one owner.                                          */
-/* [EchoCard] Fig. 2(a) (dequantize the received codes, add the own          */
-/* unquantized segment in high precision, quantize the sum once for the      */
-/* all-gather); Fig. 4 (four copies, three dequantized); abstract (the sum   */
-/* reveals the injected error); [Blog] "The cancellation rule".              */
+/* [EchoCard] Fig. 2(a) (the peers' codes are decoded, the owner's copy is  */
+/* added without quantization, and the total is quantized a single time     */
+/* before the all-gather); Fig. 4 (four copies, three of them decoded);     */
+/* abstract (the sum reveals the injected error); [Blog] "The cancellation   */
+/* rule".                                                                    */
 /* For every group of the owner's segment inside the tile:                   */
 /*   t_j = u_owner (= f32(x) + comp) when j == owner, else Q_hat(codes_j);   */
 /*   acc = t_0, then acc = acc + t_j for j = 1 .. P-1 (fp32, rank order);    */
@@ -478,7 +480,7 @@ int echo_ref_reduce_segment(const uint16_t* own_x, const float* own_comp,
 /* ------------------------------------------------------------------------ */
 /* O4: quantized all-gather and tail decode, for one rank.                   */
 /* [EchoCard] Fig. 2(a) (every rank, the owner included, decodes the same    */
-/* code); Fig. 4 (every GPU holds the same values).                          */
+/* code); Fig. 4 (after the gather all GPUs agree on the result).           */
 /* For every segment and every element of the tile inside it:               */
 /*   out[i] = Q_hat(sum codes)[i], as fp32 or as bfloat16 (nearest even).    */
 /* ------------------------------------------------------------------------ */
@@ -506,8 +508,8 @@ int echo_ref_gather_dequant(const uint8_t* sum_codes, const uint16_t* sum_params
 
 /* ------------------------------------------------------------------------ */
 /* O5: the two-timescale compensator update.                                 */
-/* [EchoCard] abstract (revealed errors are fed back into later calls so old */
-/* errors cancel); [Blog] "The cancellation rule" (a two-timescale           */
+/* [EchoCard] abstract (an error, once revealed, is returned in later      */
+/* calls and cancels); [Blog] "The cancellation rule" (a two-timescale       */
 /* compensator; each error comes back at the calls that follow).             */
 /* The pages give no equation; the reading is an error debt with a fast      */
 /* fraction alpha and a slow memory M released at rate beta:                 */

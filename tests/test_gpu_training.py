@@ -3,8 +3,8 @@ sites, P = 4, batch 32 x seq 4096 bf16 partials per rank (2^27 elements),
 forward then backward (reverse site order) per step, 100 steps = 11,200
 calls, with the two-timescale compensator (alpha = 0.5, beta = 0.25) fused
 into the kernels; each pass keeps its own compensation and slow memory,
-carried across steps (Echo paper card Fig. 1: the backward pass injects at
-the same sites; PhantomByte article, "The cancellation rule": each error
+carried across steps (Echo paper card Fig. 1: the backward pass adds its
+errors at the forward pass's sites; PhantomByte article, "The cancellation rule": each error
 returns at the calls that follow).
 
 Every call is checked bit for bit against the oracle on a row slice that

@@ -14,7 +14,7 @@
   oracle on a row slice that keeps segment ownership (the first rows of every
   segment); over the whole message the accumulated error must equal the
   outstanding error debt (-sum of comp), stay bounded with feedback, and grow
-  without it (abstract: bounded independently of depth).
+  without it (abstract: depth does not raise the bound).
 """
 import numpy as np
 import pytest

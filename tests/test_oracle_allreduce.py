@@ -1,11 +1,12 @@
 """Pins for the oracle's all-reduce call and compensator (CPU only).
 
 Structure of the call: Echo paper card, Fig. 2(a) and appendix Fig. 4 (push of
-non-owned segments as codes; the owner sums three dequantized copies and its
-own unquantized segment in high precision; the sum is quantized once; every
-rank decodes the same code); abstract (at most two quantizations per element
-for any P; the sum reveals the injected error; feeding it back cancels old
-errors; the accumulated error is bounded independently of depth).  The
+non-owned segments as codes; the owner adds three decoded copies to its own
+copy, which is never quantized, in fp32; the total is quantized a single time;
+every rank decodes the same code); abstract (no element is quantized more than
+twice, whatever P; the sum reveals the injected error; returning it cancels
+it in later calls; with feedback the accumulated error does not grow with
+depth).  The
 two-timescale compensator is named in the PhantomByte article ("The
 cancellation rule") without equations; the reading is an error debt (fast
 fraction alpha returned at the next call, slow memory released at rate beta).
@@ -101,8 +102,8 @@ def test_sum_reveals_the_injected_error(P, bits):
 
 
 def test_fig4_shaped_example():
-    """The worked example's shape (appendix Fig. 4): P = 4, b = 4, a group is
-    the two values of one segment, one-decimal inputs.  Checks what the figure
+    """The worked example's shape (appendix Fig. 4): P = 4, b = 4, each
+    segment is one group of two elements, inputs with one decimal.  Checks what the figure
     states: identical values on every rank; the owner's own copy enters the sum
     unquantized (its rank records no push error there, and the error identity
     only closes if the own copy is exact); the last row (out - sum x) is the
@@ -275,8 +276,8 @@ def test_depth_chain_closed_form(mode):
 
 
 def test_depth_chain_error_bounded_with_feedback_grows_without():
-    """Abstract: the accumulated error stays bounded independently of depth
-    with feedback, and accumulates without it (about sqrt(N) for independent
+    """Abstract: with feedback the accumulated error stays at the size of one
+    site's error however many sites there are, and without it the error piles up (about sqrt(N) for independent
     sites).  Thresholds: with classic feedback max_k RMS(E_k) <= 1.25 *
     max_k RMS(delta_k); two-timescale <= 2x; without feedback RMS(E_N) is at
     least 4x the feedback run's at N = 64."""

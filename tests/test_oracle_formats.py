@@ -1,8 +1,8 @@
 """Pins for the oracle's number-format conversions (CPU only).
 
 binary16 is where the per-group scale and zero point live (PhantomByte article
-on Echo, "The cancellation rule": half-precision quantization parameters per
-group); bfloat16 is the message format.  The oracle's converters are written
+on Echo, "The cancellation rule": each group's parameters travel at half
+precision); bfloat16 is the message format.  The oracle's converters are written
 from the IEEE 754 definitions; here they are checked against independent
 library conversions (torch's and numpy's CPU casts, both round to nearest even).
 """

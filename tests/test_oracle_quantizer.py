@@ -102,7 +102,7 @@ def check_group_brute_force(v32: np.ndarray, bits: int):
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("g", [2, 4])
 def test_brute_force_one_decimal_lattice(bits, g):
-    """Fig. 4's example quantizes groups of two values shown to one decimal;
+    """Fig. 4's example quantizes two-element groups of one-decimal values;
     sweep such groups (values k/10, |k| <= 30) exhaustively for g = 2 and at
     random for g = 4."""
     lattice = np.array([k / 10 for k in range(-30, 31)], dtype=np.float32)
