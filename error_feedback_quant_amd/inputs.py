@@ -25,7 +25,10 @@ a tensor-parallel block would produce):
             W [N, K] in bf16: "normal" draws activations N(0,1) and weights
             N(0, 1/K) (random init, so the partial sums have unit scale);
             "int" draws small integers (A in [-4, 4], W in [-3, 3]), whose
-            products and sums are exact in fp32 at any summation order.
+            products and sums are exact in fp32 at any summation order;
+            "ternary" draws A and W in {-1, 0, 1} (as int8, so that operands
+            of billions of elements fit), whose partial sums stay exact in
+            fp32 for any K below 2^24.
             Default shape: a Llama-3-8B MLP down projection at TP = 4 (4096
             tokens, hidden 4096, K = 14336 / 4 = 3584).
 
@@ -145,6 +148,10 @@ def tp_operands(rank: int, M: int, N: int, K: int, kind: str = "normal", site: i
     if kind == "int":
         a = torch.randint(-4, 5, (M, K), generator=g, device=device).to(torch.float32)
         w = torch.randint(-3, 4, (N, K), generator=g, device=device).to(torch.float32)
+    elif kind == "ternary":
+        a = torch.randint(-1, 2, (M, K), generator=g, device=device, dtype=torch.int8)
+        w = torch.randint(-1, 2, (N, K), generator=g, device=device, dtype=torch.int8)
+        return a.to(torch.bfloat16).view(torch.int16), w.to(torch.bfloat16).view(torch.int16)
     elif kind == "normal":
         a = torch.randn(M, K, generator=g, dtype=torch.float32, device=device)
         w = torch.randn(N, K, generator=g, dtype=torch.float32, device=device) * (1.0 / math.sqrt(K))

@@ -203,3 +203,29 @@ def test_fused_gemm_feeds_the_allreduce(echo, P, M):
         for r in range(P):
             assert_bits_equal(host_f32(outs_d[r]), want[r], f"output of rank {r}, call {call}")
             assert_bits_equal(host_f32(comps_d[r]), comps_h[r], f"compensation of rank {r}, call {call}")
+
+
+def test_fused_gemm_at_the_k_limit(echo):
+    """K = 2^22 - 64, the largest K the call accepts: a 256-row operand panel
+    is then 2^31 - 32 KiB bytes, the edge of the 32-bit buffer offsets of the
+    stage loads.  Two tile rows, so the second A panel starts 2 GiB into A.
+    Ternary operands keep every partial sum an integer of magnitude at most
+    K < 2^24, exact in fp32, so sampled outputs (tile corners and random
+    ones) match the oracle's matmul bit for bit."""
+    M, N = 512, 256
+    K = (1 << 22) - 64
+    say("gemm K limit", M, N, K)
+    a16, w16 = inputs.tp_operands(0, M, N, K, "ternary", device="cuda")
+    x_d = dev_u16(np.full(M * N, SENT, np.uint16))
+    echo.echo_gemm_quantize_ef(a16, w16, M, N, K, None, 1, 0, 4, 128, None, None, None, x_d, 0)
+    torch.cuda.synchronize()
+    x = host_u16(x_d).reshape(M, N)
+    rng = np.random.default_rng(77)
+    rows = [0, 255, 256, 511] + [int(v) for v in rng.integers(0, M, 4)]
+    cols = [0, 127, 128, 255] + [int(v) for v in rng.integers(0, N, 4)]
+    w_rows = {j: inputs.as_numpy_u16(w16[j:j + 1]).reshape(1, K) for j in cols}
+    for m in rows:
+        a_row = inputs.as_numpy_u16(a16[m:m + 1]).reshape(1, K)
+        for j in cols:
+            want = oracle.matmul_bf16(a_row, w_rows[j])[0]
+            assert x[m, j] == want, (m, j, hex(x[m, j]), hex(want))

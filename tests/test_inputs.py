@@ -52,6 +52,11 @@ def test_tp_operands_recipes():
     # the partial sums of a random-init layer have unit scale
     x = (A.reshape(256, 1024).astype(np.float64) @ W.reshape(128, 1024).astype(np.float64).T)
     assert 0.9 < x.std() < 1.1
+    a, w = inputs.tp_operands(2, 64, 32, 4096, "ternary")
+    A, W = f32(a.reshape(-1)), f32(w.reshape(-1))
+    assert set(np.unique(A)) == {-1.0, 0.0, 1.0} and set(np.unique(W)) == {-1.0, 0.0, 1.0}
+    assert abs(np.mean(A == 0) - 1 / 3) < 0.01
+    # |partial sum| <= K: exact in fp32 for every K below 2^24
     # seeded: the same rank gives the same draw, another rank a different one
     assert torch.equal(inputs.tp_operands(1, 8, 8, 64)[0], inputs.tp_operands(1, 8, 8, 64)[0])
     assert not torch.equal(inputs.tp_operands(1, 8, 8, 64)[0], inputs.tp_operands(2, 8, 8, 64)[0])
