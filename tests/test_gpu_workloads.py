@@ -116,6 +116,40 @@ def test_onegb_sampled_parity_and_identities(echo, P):
     torch.cuda.empty_cache()
 
 
+def test_message_beyond_2_31_elements(echo):
+    """2^31 + 2^22 elements per rank (P = 2, about 38 GB on the device):
+    every element of segment 1 lies beyond 2^31, so do its fp32 byte offsets
+    beyond 2^33, its code bytes beyond 2^30 and its parameter words beyond
+    2^24.  One call, classic feedback written in place, bf16 output, 4 tiles
+    on 2 streams.  Sampled groups, including both ends of both segments,
+    match the oracle's call on the mini message bit for bit (outputs and
+    compensations), and the two ranks' outputs agree over the whole message."""
+    P = 2
+    n = (1 << 31) + (1 << 22)
+    S = n // P
+    torch.cuda.empty_cache()
+    say("beyond 2^31", n, "generate")
+    xs = [inputs.laplace(r + 40, n, device=DEV) for r in range(P)]
+    comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, 4), dtype=torch.uint8, device=DEV)
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    idx = sample_index(P, S, 24, seed=31)
+    x_mini = [host_u16(x[idx]) for x in xs]
+    o_comps = [np.zeros(idx.numel(), np.float32) for _ in range(P)]
+    say("beyond 2^31", n, "call")
+    a = echo.make_sim_args(xs, outs, ws, bits=4, tiles=4, out_dtype=oracle.OUT_BF16, ef=True, comps=comps)
+    echo.echo_allreduce_sim(a, streams=streams)
+    torch.cuda.synchronize()
+    o_outs, _, _ = oracle.allreduce(x_mini, bits=4, ef=True, comps=o_comps, out_dtype=oracle.OUT_BF16)
+    for r in range(P):
+        assert_bits_equal(host_u16(outs[r][idx]), o_outs[r], f"out[{r}] sample")
+        assert_bits_equal(host_f32(comps[r][idx]), o_comps[r], f"comp[{r}] sample")
+    assert torch.equal(outs[1], outs[0]), "the ranks differ"
+    del xs, comps, outs, ws
+    torch.cuda.empty_cache()
+
+
 def chain_run(echo, P, n, hidden, sites, bits, gen, ef, slice_rows=16):
     """Depth chain on the GPU with per-site oracle parity on a row slice."""
     S = n // P
