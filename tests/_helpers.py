@@ -75,3 +75,54 @@ def bf16_bits_to_f64(x: np.ndarray) -> np.ndarray:
 def rand_bf16(n, seed, scale=1.0):
     rng = np.random.default_rng(seed)
     return oracle.f32_to_bf16_bits((rng.standard_normal(n) * scale).astype(np.float32))
+
+
+def chunk_slices(P: int, S: int, a: int, b: int):
+    """The element range [a, b) of every segment of a message with P segments
+    of S elements.  Concatenated in segment order they form a mini message
+    whose segment s is that range of segment s, so ownership is kept."""
+    return [slice(s * S + a, s * S + b) for s in range(P)]
+
+
+def gather_chunk(arr: np.ndarray, sl) -> np.ndarray:
+    return np.concatenate([arr[q] for q in sl])
+
+
+def oracle_by_chunks(xs, comps, P, L, out_dtype, workers, visit, bits=4):
+    """The oracle's whole call (classic feedback written in place when comps
+    is given, else feedback off) over a message of P segments, computed as
+    independent calls on mini messages made of the same L-element range of
+    every segment.  Quantization, the owner's sum and the feedback act per
+    group and per element, and every range holds whole groups, so the
+    results are those of one call on the whole message.  The calls run in
+    `workers` host threads (the oracle's C entry point releases the GIL).
+    `comps` is the state before the call and is left untouched.
+    visit(slices, outs, comps_after) runs in the worker for each chunk and
+    returns None or a description of the first mismatch; the first such
+    description is returned."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = xs[0].size
+    S = n // P
+    assert S % L == 0 and L % 128 == 0
+
+    def one(a):
+        sl = chunk_slices(P, S, a, a + L)
+        xm = [gather_chunk(x, sl) for x in xs]
+        cm = [gather_chunk(c, sl) for c in comps] if comps is not None else None
+        outs, _, _ = oracle.allreduce(xm, bits=bits, ef=comps is not None, comps=cm, out_dtype=out_dtype)
+        return visit(sl, outs, cm)
+
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for res in pool.map(one, range(0, S, L)):
+            if res is not None:
+                return res
+    return None
+
+
+def host_workers(cap: int = 16) -> int:
+    import os
+    try:
+        return max(1, min(cap, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(cap, os.cpu_count() or 1))

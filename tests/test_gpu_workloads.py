@@ -1,9 +1,11 @@
 """The workloads at full size on the GPU.
 
 * 1 GiB message (2^29 bf16 per rank, Laplace(0,1)), P = 4 and P = 8, in the
-  launch configuration the benchmark times (bf16 output, classic feedback
-  written in place, tiles staggered over four streams), two consecutive
-  calls.  Sampled parity: the oracle recomputes a set of groups from every
+  launch configurations the benchmark times (bf16 output, classic feedback
+  written in place; one tile per segment on one stream, and tiles staggered
+  over four streams), two consecutive calls.  Full parity: every output and
+  compensation element against the oracle's whole call, run in host threads
+  over ranges that keep segment ownership.  Sampled parity: the oracle recomputes a set of groups from every
   segment (an exact sub-problem: quantization, sums and feedback act per
   group and per element) and must match bit for bit; properties over the
   whole message: bitwise identical outputs on every rank, and the injected
@@ -16,12 +18,15 @@
   outstanding error debt (-sum of comp), stay bounded with feedback, and grow
   without it (abstract: depth does not raise the bound).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from _helpers import DEV, assert_bits_equal, host_f32, host_u16, say
+from _helpers import (DEV, assert_bits_equal, gather_chunk, host_f32, host_u16, host_workers,
+                      oracle_by_chunks, say)
 from error_feedback_quant_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -113,6 +118,58 @@ def test_onegb_sampled_parity_and_identities(echo, P):
             del out, u_sum, mag, e_sum
         del c_before
     del xs, comps, outs, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("P", [4, 8])
+def test_onegb_full_parity(echo, P):
+    """Every element of the 1 GiB message (2^29 bf16 per rank, Laplace(0,1)),
+    P = 4 and P = 8, bit for bit against the oracle's whole call: all P bf16
+    outputs and all P compensations.  Two calls carry the feedback: the
+    first in the headline schedule (one tile per segment on one stream), the
+    second staged (8 tiles on 4 streams).  The oracle's call runs on the host
+    as independent calls on mini messages made of the same range of every
+    segment, in threads (its chunked form is pinned to one whole call on the
+    CPU)."""
+    n = 1 << 29
+    S = n // P
+    L = 1 << 18
+    workers = host_workers()
+    torch.cuda.empty_cache()
+    comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+    outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, 4), dtype=torch.uint8, device=DEV)
+    c_host = [np.zeros(n, np.float32) for _ in range(P)]      # state before the call
+    for call, (tiles, nstreams) in enumerate([(1, 1), (8, 4)]):
+        say("onegb full", P, "call", call, "generate")
+        xs = [inputs.laplace(r + 16 * call, n, device=DEV) for r in range(P)]
+        xh = [host_u16(x) for x in xs]
+        streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+        say("onegb full", P, "call", call, "tiles", tiles, "streams", nstreams)
+        a = echo.make_sim_args(xs, outs, ws, bits=4, tiles=tiles, out_dtype=oracle.OUT_BF16, ef=True,
+                               comps=comps)
+        echo.echo_allreduce_sim(a, streams=streams)
+        torch.cuda.synchronize()
+        out_h = [host_u16(o) for o in outs]
+        c_after = [host_f32(c) for c in comps]
+        del xs
+
+        def visit(sl, o_outs, o_comps):
+            for r in range(P):
+                if gather_chunk(out_h[r], sl).tobytes() != o_outs[r].tobytes():
+                    return f"P={P} call {call}: out[{r}] differs in the range at {sl[0].start} of segment 0"
+                if gather_chunk(c_after[r], sl).tobytes() != o_comps[r].tobytes():
+                    return f"P={P} call {call}: comp[{r}] differs in the range at {sl[0].start} of segment 0"
+            return None
+
+        say("onegb full", P, "call", call, "oracle on", workers, "threads")
+        t0 = time.time()
+        bad = oracle_by_chunks(xh, c_host, P, L, oracle.OUT_BF16, workers, visit)
+        print(f"onegb full P={P} call {call}: oracle and compare {time.time() - t0:.1f} s", flush=True)
+        assert bad is None, bad
+        del xh, out_h
+        c_host = c_after
+    del comps, outs, ws, c_host
     torch.cuda.empty_cache()
 
 

@@ -315,3 +315,38 @@ def test_argument_checks():
                                kw["bits"], kw["group"], codes, params, None)
     with pytest.raises(oracle.OracleError):   # n not a multiple of P * g
         oracle.quantize_ef(x, None, n - 128, P, 0, 0, 0, 4, 128, codes, params, None)
+
+
+@pytest.mark.parametrize("P,bits,out_dtype", [(4, 4, oracle.OUT_BF16), (8, 4, oracle.OUT_BF16), (3, 8, oracle.OUT_F32)])
+def test_chunked_calls_equal_one_whole_call(P, bits, out_dtype):
+    """The full-size GPU parity test computes the oracle's call as
+    independent calls on mini messages made of the same range of every
+    segment, in host threads.  That is valid because quantization, the
+    owner's sum and the feedback act per group and per element: here the
+    chunked result must equal one call on the whole message, bit for bit,
+    with a nonzero compensation carried in and written back."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from _helpers import oracle_by_chunks, gather_chunk
+
+    S = 128 * 24
+    n = P * S
+    rng = np.random.default_rng(7 + P)
+    xs = [oracle.f32_to_bf16_bits(rng.laplace(size=n).astype(np.float32)) for _ in range(P)]
+    comps0 = [(rng.standard_normal(n) * 0.05).astype(np.float32) for _ in range(P)]
+    kept = [c.copy() for c in comps0]
+    whole_c = [c.copy() for c in comps0]
+    whole, _, _ = oracle.allreduce(xs, bits=bits, ef=True, comps=whole_c, out_dtype=out_dtype)
+
+    def visit(sl, outs, cm):
+        for r in range(P):
+            if gather_chunk(whole[r], sl).tobytes() != outs[r].tobytes():
+                return f"out[{r}] at {sl[0].start}"
+            if gather_chunk(whole_c[r], sl).tobytes() != cm[r].tobytes():
+                return f"comp[{r}] at {sl[0].start}"
+        return None
+
+    for L in (128, 384, 128 * 8):
+        assert oracle_by_chunks(xs, comps0, P, L, out_dtype, 4, visit, bits=bits) is None, L
+    # the chunked call leaves its input state untouched
+    assert all(c.tobytes() == k.tobytes() for c, k in zip(comps0, kept))
