@@ -88,18 +88,20 @@ def gather_chunk(arr: np.ndarray, sl) -> np.ndarray:
     return np.concatenate([arr[q] for q in sl])
 
 
-def oracle_by_chunks(xs, comps, P, L, out_dtype, workers, visit, bits=4):
-    """The oracle's whole call (classic feedback written in place when comps
-    is given, else feedback off) over a message of P segments, computed as
+def oracle_by_chunks(xs, comps, P, L, out_dtype, workers, visit, bits=4, slows=None, alpha=1.0,
+                     beta=0.0):
+    """The oracle's whole call over a message of P segments, computed as
     independent calls on mini messages made of the same L-element range of
-    every segment.  Quantization, the owner's sum and the feedback act per
-    group and per element, and every range holds whole groups, so the
-    results are those of one call on the whole message.  The calls run in
-    `workers` host threads (the oracle's C entry point releases the GIL).
-    `comps` is the state before the call and is left untouched.
-    visit(slices, outs, comps_after) runs in the worker for each chunk and
-    returns None or a description of the first mismatch; the first such
-    description is returned."""
+    every segment.  Feedback is on when `comps` is given (classic, written
+    in place, for alpha = 1 and beta = 0; otherwise two-timescale with the
+    slow memories `slows`), else off.  Quantization, the owner's sum and the
+    feedback act per group and per element, and every range holds whole
+    groups, so the results are those of one call on the whole message.  The
+    calls run in `workers` host threads (the oracle's C entry point releases
+    the GIL).  `comps` and `slows` are the state before the call and are
+    left untouched.  visit(slices, outs, comps_after, slows_after) runs in
+    the worker for each chunk and returns None or a description of the
+    first mismatch; the first such description is returned."""
     from concurrent.futures import ThreadPoolExecutor
 
     n = xs[0].size
@@ -110,8 +112,10 @@ def oracle_by_chunks(xs, comps, P, L, out_dtype, workers, visit, bits=4):
         sl = chunk_slices(P, S, a, a + L)
         xm = [gather_chunk(x, sl) for x in xs]
         cm = [gather_chunk(c, sl) for c in comps] if comps is not None else None
-        outs, _, _ = oracle.allreduce(xm, bits=bits, ef=comps is not None, comps=cm, out_dtype=out_dtype)
-        return visit(sl, outs, cm)
+        sm = [gather_chunk(m, sl) for m in slows] if slows is not None else None
+        outs, _, _ = oracle.allreduce(xm, bits=bits, ef=comps is not None, alpha=alpha, beta=beta,
+                                      comps=cm, slows=sm, out_dtype=out_dtype)
+        return visit(sl, outs, cm, sm)
 
     with ThreadPoolExecutor(max_workers=workers) as pool:
         for res in pool.map(one, range(0, S, L)):

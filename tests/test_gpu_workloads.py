@@ -12,11 +12,12 @@
   error equals the revealed errors (fed back as -comp) up to fp32 rounding.
 * Depth chains (Echo paper card Fig. 1: N injection sites add their
   all-reduce output to the hidden state): 4-bit, P = 4, 2048 x 4096, 64 sites,
-  and 8-bit, P = 4, 4096 x 1024, 56 sites.  Each site is checked against the
-  oracle on a row slice that keeps segment ownership (the first rows of every
-  segment); over the whole message the accumulated error must equal the
-  outstanding error debt (-sum of comp), stay bounded with feedback, and grow
-  without it (abstract: depth does not raise the bound).
+  and 8-bit, P = 4, 4096 x 1024, 56 sites, with classic feedback and without
+  it; the 4-bit chain also with the two-timescale compensator.  Every site's
+  call is checked against the oracle's whole call over the whole message,
+  bit for bit; the accumulated error must equal the outstanding error debt,
+  stay bounded with feedback, and grow without it (abstract: depth does not
+  raise the bound).
 """
 import time
 
@@ -154,7 +155,7 @@ def test_onegb_full_parity(echo, P):
         c_after = [host_f32(c) for c in comps]
         del xs
 
-        def visit(sl, o_outs, o_comps):
+        def visit(sl, o_outs, o_comps, _):
             for r in range(P):
                 if gather_chunk(out_h[r], sl).tobytes() != o_outs[r].tobytes():
                     return f"P={P} call {call}: out[{r}] differs in the range at {sl[0].start} of segment 0"
@@ -207,19 +208,24 @@ def test_message_beyond_2_31_elements(echo):
     torch.cuda.empty_cache()
 
 
-def chain_run(echo, P, n, hidden, sites, bits, gen, ef, slice_rows=16):
-    """Depth chain on the GPU with per-site oracle parity on a row slice."""
+def chain_run(echo, P, n, sites, bits, gen, mode, alpha=1.0, beta=0.0):
+    """Depth chain on the GPU.  Every site's call is checked bit for bit
+    against the oracle's whole call over the whole message: the fp32
+    outputs of all ranks, the compensations and the slow memories.  The
+    oracle takes as its state before each call the GPU's state after the
+    previous one, which the previous site has just matched bit for bit."""
     S = n // P
-    rows_per_seg = S // hidden
-    assert rows_per_seg >= slice_rows
-    idx = (torch.arange(P, device=DEV)[:, None] * S +
-           torch.arange(slice_rows * hidden, device=DEV)[None, :]).reshape(-1)
-    mini_n = idx.numel()
+    ef = mode != "off"
+    two = mode == "two_timescale"
     comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if ef else None
+    slows = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if two else None
     outs = [torch.empty(n, dtype=torch.float32, device=DEV) for _ in range(P)]
     ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
     streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
-    o_comps = [np.zeros(mini_n, np.float32) for _ in range(P)] if ef else None
+    c_host = [np.zeros(n, np.float32) for _ in range(P)] if ef else None
+    s_host = [np.zeros(n, np.float32) for _ in range(P)] if two else None
+    workers = host_workers()
+    L = min(S, 1 << 16)
     h = torch.zeros(n, dtype=torch.float64, device=DEV)
     h_exact = torch.zeros(n, dtype=torch.float64, device=DEV)
     rms = lambda t: float(torch.sqrt(torch.mean(t * t)))
@@ -227,7 +233,8 @@ def chain_run(echo, P, n, hidden, sites, bits, gen, ef, slice_rows=16):
     for k in range(sites):
         xs = [gen(r, k) for r in range(P)]
         c_sum = sum(c.double() for c in comps) if ef else 0.0
-        a = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=4, out_dtype=oracle.OUT_F32, ef=ef, comps=comps)
+        a = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=4, out_dtype=oracle.OUT_F32, ef=ef,
+                               alpha=alpha, beta=beta, comps=comps, slows=slows)
         echo.echo_allreduce_sim(a, streams=streams)
         x_sum = sum(x.view(torch.bfloat16).double() for x in xs)
         out = outs[0].double()
@@ -238,25 +245,38 @@ def chain_run(echo, P, n, hidden, sites, bits, gen, ef, slice_rows=16):
         d_rms.append(rms(out - x_sum - c_sum))
         if ef:
             debt = -sum(c.double() for c in comps)
+            if two:
+                debt += sum(m.double() for m in slows)
             debt_gap.append(float((E - debt).abs().max()) / max(float(E.abs().max()), 1e-30))
-        # per-site parity on the slice
-        x_mini = [host_u16(x[idx]) for x in xs]
-        o_outs, _, _ = oracle.allreduce(x_mini, bits=bits, ef=ef, comps=o_comps, out_dtype=oracle.OUT_F32)
-        for r in range(P):
-            assert_bits_equal(host_f32(outs[r][idx]), o_outs[r], f"site {k} out[{r}] slice")
-        if ef:
-            for r in range(P):
-                assert_bits_equal(host_f32(comps[r][idx]), o_comps[r], f"site {k} comp[{r}] slice")
         for r in range(1, P):
             assert torch.equal(outs[r], outs[0])
-        del xs, x_sum, out, E
-    del comps, outs, ws, h, h_exact
+        # whole-message parity at this site
+        xh = [host_u16(x) for x in xs]
+        out_h = [host_f32(o) for o in outs]
+        c_after = [host_f32(c) for c in comps] if ef else None
+        s_after = [host_f32(m) for m in slows] if two else None
+
+        def visit(sl, o_outs, o_c, o_s):
+            for r in range(P):
+                if gather_chunk(out_h[r], sl).tobytes() != o_outs[r].tobytes():
+                    return f"out[{r}] differs in the range at {sl[0].start} of segment 0"
+                if ef and gather_chunk(c_after[r], sl).tobytes() != o_c[r].tobytes():
+                    return f"comp[{r}] differs in the range at {sl[0].start} of segment 0"
+                if two and gather_chunk(s_after[r], sl).tobytes() != o_s[r].tobytes():
+                    return f"slow[{r}] differs in the range at {sl[0].start} of segment 0"
+            return None
+
+        bad = oracle_by_chunks(xh, c_host, P, L, oracle.OUT_F32, workers, visit, bits=bits, slows=s_host,
+                               alpha=alpha, beta=beta)
+        assert bad is None, f"{mode} site {k}: {bad}"
+        c_host, s_host = c_after, s_after
+        del xs, x_sum, out, E, xh, out_h
+    del comps, slows, outs, ws, h, h_exact
     torch.cuda.empty_cache()
     return np.array(E_rms), np.array(d_rms), np.array(debt_gap)
 
 
-@pytest.mark.parametrize("which", ["chain", "chain8"])
-def test_depth_chain_bounded_with_feedback(echo, which):
+def chain_gen(which):
     if which == "chain":
         P, tokens, hidden, sites, bits = 4, 2048, 4096, 64, 4
         sigma = inputs.chain_channel_scale(hidden, device=DEV)
@@ -264,11 +284,16 @@ def test_depth_chain_bounded_with_feedback(echo, which):
     else:
         P, tokens, hidden, sites, bits = 4, 4096, 1024, 56, 8
         gen = lambda r, k: inputs.chain8(r, k, tokens, hidden, device=DEV)
-    n = tokens * hidden
+    return P, tokens * hidden, sites, bits, gen
+
+
+@pytest.mark.parametrize("which", ["chain", "chain8"])
+def test_depth_chain_bounded_with_feedback(echo, which):
+    P, n, sites, bits, gen = chain_gen(which)
     say(which, "with feedback")
-    E_ef, d_ef, gap = chain_run(echo, P, n, hidden, sites, bits, gen, ef=True)
+    E_ef, d_ef, gap = chain_run(echo, P, n, sites, bits, gen, "classic")
     say(which, "without feedback")
-    E_off, d_off, _ = chain_run(echo, P, n, hidden, sites, bits, gen, ef=False)
+    E_off, d_off, _ = chain_run(echo, P, n, sites, bits, gen, "off")
     print(f"{which}: max RMS E with EF {E_ef.max():.3e}, max RMS delta {d_ef.max():.3e}, "
           f"RMS E_N without EF {E_off[-1]:.3e}, ratio {E_off[-1] / E_ef[-1]:.2f}, max debt gap {gap.max():.2e}",
           flush=True)
@@ -279,3 +304,21 @@ def test_depth_chain_bounded_with_feedback(echo, which):
     # accumulates without feedback
     assert E_off[-1] >= 4.0 * E_ef[-1]
     assert E_off[-1] > 1.5 * E_off[sites // 4]
+
+
+def test_depth_chain_two_timescale(echo):
+    """The 4-bit chain (64 sites, 2048 x 4096, P = 4) with the two-timescale
+    compensator (alpha = 0.5, beta = 0.25) fused into push and reduce: the
+    accumulated error equals the outstanding debt sum_j (M_j - c_j) at every
+    site and stays within twice the largest injected error, independent of
+    depth (PhantomByte article, "The cancellation rule": each error returns
+    at the calls that follow)."""
+    P, n, sites, bits, gen = chain_gen("chain")
+    say("chain two-timescale")
+    E, d, gap = chain_run(echo, P, n, sites, bits, gen, "two_timescale", alpha=0.5, beta=0.25)
+    print(f"chain two-timescale: max RMS E {E.max():.3e}, max RMS delta {d.max():.3e}, "
+          f"ratio {E.max() / d.max():.3f}, max debt gap {gap.max():.2e}", flush=True)
+    assert gap.max() < 1e-3
+    assert E.max() <= 2.0 * d.max()
+    # the bound does not grow with depth: the second half is no worse than 1.1x the first
+    assert E[sites // 2:].max() <= 1.1 * E[:sites // 2].max()

@@ -338,7 +338,14 @@ def test_chunked_calls_equal_one_whole_call(P, bits, out_dtype):
     whole_c = [c.copy() for c in comps0]
     whole, _, _ = oracle.allreduce(xs, bits=bits, ef=True, comps=whole_c, out_dtype=out_dtype)
 
-    def visit(sl, outs, cm):
+    slows0 = [(rng.standard_normal(n) * 0.02).astype(np.float32) for _ in range(P)]
+    kept_s = [m.copy() for m in slows0]
+    two_c = [c.copy() for c in comps0]
+    two_s = [m.copy() for m in slows0]
+    two, _, _ = oracle.allreduce(xs, bits=bits, ef=True, alpha=0.5, beta=0.25, comps=two_c, slows=two_s,
+                                 out_dtype=out_dtype)
+
+    def visit(sl, outs, cm, sm):
         for r in range(P):
             if gather_chunk(whole[r], sl).tobytes() != outs[r].tobytes():
                 return f"out[{r}] at {sl[0].start}"
@@ -346,7 +353,20 @@ def test_chunked_calls_equal_one_whole_call(P, bits, out_dtype):
                 return f"comp[{r}] at {sl[0].start}"
         return None
 
+    def visit_two(sl, outs, cm, sm):
+        for r in range(P):
+            if gather_chunk(two[r], sl).tobytes() != outs[r].tobytes():
+                return f"out[{r}] at {sl[0].start}"
+            if gather_chunk(two_c[r], sl).tobytes() != cm[r].tobytes():
+                return f"comp[{r}] at {sl[0].start}"
+            if gather_chunk(two_s[r], sl).tobytes() != sm[r].tobytes():
+                return f"slow[{r}] at {sl[0].start}"
+        return None
+
     for L in (128, 384, 128 * 8):
         assert oracle_by_chunks(xs, comps0, P, L, out_dtype, 4, visit, bits=bits) is None, L
-    # the chunked call leaves its input state untouched
+        assert oracle_by_chunks(xs, comps0, P, L, out_dtype, 4, visit_two, bits=bits, slows=slows0,
+                                alpha=0.5, beta=0.25) is None, L
+    # the chunked calls leave their input state untouched
     assert all(c.tobytes() == k.tobytes() for c, k in zip(comps0, kept))
+    assert all(m.tobytes() == k.tobytes() for m, k in zip(slows0, kept_s))
