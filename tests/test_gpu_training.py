@@ -9,7 +9,9 @@ returns at the calls that follow).
 
 Every call is checked bit for bit against the oracle on a row slice that
 keeps segment ownership (the first row of every segment: an exact
-sub-problem); the state must stay bounded over the whole message, and within
+sub-problem); four calls spread over the run (the first forward and first
+backward call, one in the middle, the last) are checked over the whole
+message against the oracle's whole call from the GPU's state before them; the state must stay bounded over the whole message, and within
 each pass the accumulated error must equal the change of the outstanding
 error debt (checked over the whole message every 25 steps).
 """
@@ -20,7 +22,8 @@ import pytest
 import torch
 
 import oracle
-from _helpers import DEV, assert_bits_equal, host_f32, host_u16, say
+from _helpers import (DEV, assert_bits_equal, gather_chunk, host_f32, host_u16, host_workers,
+                      oracle_by_chunks, say)
 from error_feedback_quant_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +33,32 @@ SITES = 2 * LAYERS
 N = 32 * 4096 * HIDDEN                 # per rank
 STEPS = int(os.environ.get("ECHO_TRAINING_STEPS", "100"))
 ALPHA, BETA = 0.5, 0.25
+# (step, pass, site) of the calls checked over the whole message
+FULL = {(0, "fwd", 0), (0, "bwd", SITES - 1), (STEPS // 2, "fwd", LAYERS), (STEPS - 1, "bwd", 0)}
+
+
+def full_call_parity(xs, outs, c_before, s_before, comps, slows, what):
+    """One call over the whole message against the oracle's whole call, run
+    in host threads over ranges that keep segment ownership: bf16 outputs of
+    all ranks, compensations and slow memories, bit for bit."""
+    xh = [host_u16(x) for x in xs]
+    out_h = [host_u16(o) for o in outs]
+    c_after = [host_f32(c) for c in comps]
+    s_after = [host_f32(m) for m in slows]
+
+    def visit(sl, o_outs, o_c, o_s):
+        for r in range(P):
+            if gather_chunk(out_h[r], sl).tobytes() != o_outs[r].tobytes():
+                return f"out[{r}] differs in the range at {sl[0].start} of segment 0"
+            if gather_chunk(c_after[r], sl).tobytes() != o_c[r].tobytes():
+                return f"comp[{r}] differs in the range at {sl[0].start} of segment 0"
+            if gather_chunk(s_after[r], sl).tobytes() != o_s[r].tobytes():
+                return f"slow[{r}] differs in the range at {sl[0].start} of segment 0"
+        return None
+
+    bad = oracle_by_chunks(xh, c_before, P, 1 << 18, oracle.OUT_BF16, host_workers(), visit, bits=4,
+                           slows=s_before, alpha=ALPHA, beta=BETA)
+    assert bad is None, f"{what}: {bad}"
 
 
 def test_training_workload_two_timescale(tmp_path):
@@ -57,9 +86,17 @@ def test_training_workload_two_timescale(tmp_path):
             for site in sites:
                 xs = [inputs.training(r, step, site + (SITES if p == "bwd" else 0), p == "bwd", N, device=DEV)
                       for r in range(P)]
+                full = (step, p, site) in FULL
+                if full:
+                    c_before = [host_f32(c) for c in comps]
+                    s_before = [host_f32(m) for m in slows]
                 a = echo.make_sim_args(xs, outs, ws, bits=4, tiles=1, out_dtype=echo.OUT_BF16, ef=True,
                                        alpha=ALPHA, beta=BETA, comps=comps, slows=slows)
                 echo.echo_allreduce_sim(a)
+                if full:
+                    say(f"step {step} {p} site {site}: whole-message parity")
+                    full_call_parity(xs, outs, c_before, s_before, comps, slows, f"step {step} {p} site {site}")
+                    del c_before, s_before
                 x_mini = [host_u16(x[idx]) for x in xs]
                 o_outs, _, _ = oracle.allreduce(x_mini, bits=4, ef=True, alpha=ALPHA, beta=BETA, comps=oc,
                                                 slows=os_, errs=oe, out_dtype=oracle.OUT_BF16)
