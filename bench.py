@@ -26,9 +26,10 @@ Also printed (same JSON line):
   staged        the same call with tiles staggered across streams.
   variants      the same call with Table 8's ablation quantizers (naive zero
                 point, symmetric grid) and with groups of 256.
-  modes         the same call with feedback off, with fp32 output, and with
+  modes         the same call with feedback off, with fp32 output, with
                 the two-timescale compensator fused into push and reduce
-                (B then counts 16 bytes of state traffic instead of 8).
+                (B then counts 16 bytes of state traffic instead of 8), and
+                with the other code width (8-bit codes: k_b = 1.03125).
   tp_block      one rank's row-parallel matmul with the entry pass fused in
                 its epilogue (echo_gemm_quantize_ef) against hipBLASLt +
                 echo_quantize_ef, at the Llama-3-8B down projection (TP = 4),
@@ -364,14 +365,17 @@ def main():
                               "frac_of_peak": round(rv["value"] / HBM_PEAK_GBS, 4)}
     modes = None
     if not a.no_modes:
-        # the same call with feedback off, with fp32 output, and with the
+        # the same call with feedback off, with fp32 output, with the
         # two-timescale compensator (alpha = 0.5, beta = 0.25) fused into the
-        # push and the reduce
+        # push and the reduce, and with 8-bit codes
         modes = {}
-        for name, m_ef, m_bf16, alpha, beta in (("ef_off", False, out_bf16, 1.0, 0.0),
-                                                ("f32_out", ef, False, 1.0, 0.0),
-                                                ("two_timescale", True, out_bf16, 0.5, 0.25)):
-            rm = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 3),
+        other_bits = 8 if a.bits == 4 else 4
+        for name, m_ef, m_bf16, alpha, beta, m_bits in (
+                ("ef_off", False, out_bf16, 1.0, 0.0, a.bits),
+                ("f32_out", ef, False, 1.0, 0.0, a.bits),
+                ("two_timescale", True, out_bf16, 0.5, 0.25, a.bits),
+                (f"bits{other_bits}", ef, out_bf16, 1.0, 0.0, other_bits)):
+            rm = run_case(echo, torch, inputs, a.P, N_1GIB, m_bits, a.tiles, a.streams, max(5, a.steps // 3),
                           a.warmup, m_bf16, m_ef, time_kernel=False, alpha=alpha, beta=beta)
             modes[name] = {"value": round(rm["value"], 1), "ms_per_step": round(rm["ms_per_step"], 4),
                            "bytes_per_elem_per_rank": round(rm["B"], 5),

@@ -60,16 +60,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #ifndef ECHO_NT
 #define ECHO_NT 1
 #endif
+#ifndef ECHO_NT_LD
+#define ECHO_NT_LD ECHO_NT
+#endif
+#ifndef ECHO_NT_ST
+#define ECHO_NT_ST ECHO_NT
+#endif
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p)
 {
-    if constexpr (ECHO_NT) return __builtin_nontemporal_load(p);
+    if constexpr (ECHO_NT_LD) return __builtin_nontemporal_load(p);
     else return *p;
 }
 template <typename T>
 __device__ __forceinline__ void st_stream(T* p, const T& v)
 {
-    if constexpr (ECHO_NT) __builtin_nontemporal_store(v, p);
+    if constexpr (ECHO_NT_ST) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
 // the tail's decoded output (write-only stream)
