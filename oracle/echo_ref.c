@@ -37,7 +37,12 @@
  *     newest error is returned at the next call, the rest enters a slow
  *     memory M that is released at rate beta per call.
  *
- * Parity status of each function is stated at its definition.
+ * Parity status of each function is stated at its definition.  Parity
+ * unpinned: the two-timescale compensator's constants and its exact update
+ * equation (the pages name the compensator and where it runs, and print
+ * neither), and the values of appendix Fig. 4 (not in the text).  Everything
+ * else is pinned by the CPU tests against library conversions, exact
+ * arithmetic, brute force over all codes, closed forms and invariants.
  */
 #include <math.h>
 #include <stdint.h>
