@@ -377,6 +377,26 @@ __device__ __forceinline__ void decode8(const float* q, uint32_t word, float* v)
     for (int i = 0; i < 8; ++i) v[i] = (q[i] - zf) * s;
 }
 
+// The same decode where the zero point is an integer (zero-aware and
+// symmetric quantizers): z <= 255 and s is a binary16 value (11 significant
+// bits), so z*s, q*s and their difference (q - z)*s all fit in 19 bits and
+// are exact in fp32; one fma q*s + (-(z*s)) then rounds an exact,
+// representable value and gives the bits of the two-step form, +0 included
+// when q == z.  The naive quantizer's zero point carries a fraction, so
+// there q - z can round and only the two-step form is right.
+template <int QUANT>
+__device__ __forceinline__ void decode8_q(const float* q, uint32_t word, float* v)
+{
+    if constexpr (QUANT == kNaive) {
+        decode8(q, word, v);
+    } else {
+        const float s = f16_bits_to_f32(word & 0xFFFFu);
+        const float nzs = -(f16_bits_to_f32(word >> 16) * s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(q[i], s, nzs);
+    }
+}
+
 // Quantize the lane's 8 values of one group (the whole group cooperates),
 // store codes and parameters, and return the codes (as integer-valued floats)
 // in q and the group's parameters.  `lane` is the lane within the wavefront.
@@ -726,7 +746,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
             } else {
                 float q[8], t[8];
                 pk[k][j].unpack(q);
-                decode8(q, pw[k][j], t);
+                decode8_q<QUANT>(q, pw[k][j], t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? t[i] : acc[i] + t[i];
             }

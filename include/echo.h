@@ -146,8 +146,10 @@ int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P
  *
  *   own_x_bf16, own_comp (device, in)  the owner's x and comp (comp nullable)
  *   peer_codes, peer_params (host arrays of P device pointers, in)
- *                                      each rank's push codes/params; entry
- *                                      [owner] is not read and may be NULL
+ *                                      each rank's push codes/params, made by
+ *                                      echo_quantize_ef with the same
+ *                                      quantizer flag; entry [owner] is not
+ *                                      read and may be NULL
  *   sum_codes, sum_params (device, out) message-shaped; only segment `owner`
  *                                      inside the tile is written
  *   own_err (device, out, nullable)    fp32 [n]; may alias own_comp
