@@ -64,8 +64,9 @@ int check_common(int64_t n, int P, int64_t tile_begin, int64_t tile_len, int bit
     if (group != 128 && group != 256) return ECHO_EUNSUP;
     if (n < 0 || n > kMaxN || n % ((int64_t)P * group) != 0) return ECHO_ESHAPE;
     const int64_t S = n / P;
-    if (tile_begin < 0 || tile_len < 0 || tile_begin % group || tile_len % group ||
-        tile_begin + tile_len > S)
+    // tile_begin + tile_len could overflow for huge arguments: compare by subtraction
+    if (tile_begin < 0 || tile_len < 0 || tile_begin % group || tile_len % group || tile_begin > S ||
+        tile_len > S - tile_begin)
         return ECHO_ESHAPE;
     return ECHO_OK;
 }

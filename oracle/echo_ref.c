@@ -352,7 +352,7 @@ static int check_shape(int64_t n, int P, int64_t tile_begin, int64_t tile_len,
     if (n < 0 || tile_begin < 0 || tile_len < 0) return REF_ESHAPE;
     if (n % ((int64_t)P * g) != 0) return REF_ESHAPE;
     int64_t S = n / P;
-    if (tile_begin % g || tile_len % g || tile_begin + tile_len > S) return REF_ESHAPE;
+    if (tile_begin % g || tile_len % g || tile_begin > S || tile_len > S - tile_begin) return REF_ESHAPE;
     return REF_OK;
 }
 

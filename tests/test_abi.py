@@ -60,6 +60,8 @@ def test_quantize_ef_argument_checks():
     assert q(n=n + 128) == echo.ESHAPE and q(n=-512) == echo.ESHAPE
     assert q(tb=64) == echo.ESHAPE and q(tl=100) == echo.ESHAPE
     assert q(tb=1024, tl=128) == echo.ESHAPE          # past the segment end (S = 1024)
+    big = (1 << 63) - 128                               # a multiple of 128 near INT64_MAX
+    assert q(tb=big, tl=big) == echo.ESHAPE and q(tb=128, tl=big) == echo.ESHAPE
     assert q(x=None) == echo.EINVAL and q(codes=None) == echo.EINVAL
     assert q(x=FAKE + 8) == echo.EALIGN and q(comp=FAKE + 4) == echo.EALIGN
     assert q(flags=8) == echo.EINVAL and q(flags=6) == echo.EINVAL   # unknown bit; both ablations
