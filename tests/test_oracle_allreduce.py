@@ -370,3 +370,42 @@ def test_chunked_calls_equal_one_whole_call(P, bits, out_dtype):
     # the chunked calls leave their input state untouched
     assert all(c.tobytes() == k.tobytes() for c, k in zip(comps0, kept))
     assert all(m.tobytes() == k.tobytes() for m, k in zip(slows0, kept_s))
+
+
+@pytest.mark.parametrize("alpha,beta", [(0.5, 0.25), (0.75, 0.1)])
+def test_two_timescale_error_bound_independent_of_depth(alpha, beta):
+    """Elementwise bound for the two-timescale compensator: each rank's
+    outstanding debt M - c stays within (1 + (1 - alpha) / beta) * max|e|
+    (the slow memory is a geometric sum of (1 - alpha) e with ratio 1 - beta;
+    the fast part returns alpha e + beta M), so the accumulated error over a
+    chain, the sum of the P debts, stays within P (1 + (1 - alpha) / beta)
+    max|e| at every depth, where max|e| runs over every error injected so
+    far.  The e_j come from the unfused form (errors written out, then the
+    compensator)."""
+    P, tokens, hidden, N = 4, 8, 512, 64
+    n = tokens * hidden
+    sigma = inputs.chain_channel_scale(hidden)
+    part = _chain_partials(P, tokens, hidden, N, sigma)
+    comps = [np.zeros(n, np.float32) for _ in range(P)]
+    slows = [np.zeros(n, np.float32) for _ in range(P)]
+    errs = [np.zeros(n, np.float32) for _ in range(P)]
+    h = np.zeros(n)
+    h_exact = np.zeros(n)
+    emax = 0.0
+    factor = P * (1.0 + (1.0 - alpha) / beta)
+    worst = 0.0
+    for k in range(N):
+        xs = part(k)
+        outs, _, _ = oracle.allreduce(xs, bits=4, ef=True, alpha=alpha, beta=beta, comps=comps,
+                                      slows=slows, errs=errs)
+        emax = max(emax, max(float(np.abs(e).max()) for e in errs))
+        h += outs[0].astype(np.float64)
+        for x in xs:
+            h_exact += bf16_to_f64(x)
+        E = np.abs(h - h_exact)
+        # fp32 roundings of the update and of the sums: a relative slack far above their size
+        slack = (k + 1) * 64 * (P + 3) * U24 * (np.abs(h).max() + 1.0)
+        assert E.max() <= factor * emax * (1 + 1e-5) + slack, (k, E.max(), factor * emax)
+        worst = max(worst, E.max() / (factor * emax))
+    # the bound is not vacuous: the chain uses a sizeable part of it
+    assert worst > 0.05
