@@ -304,7 +304,20 @@ def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=4):
     B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4)
     return {"value": round(P * m * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"one call on {m} of {n} elements per rank (1/{frac_den} of every segment, "
-                      f"same distribution), P={P}, {dt:.2f} s single-threaded"}
+                      f"same distribution), P={P}, {dt:.2f} s single-threaded",
+            "cpu": host_cpu_model()}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
