@@ -409,3 +409,34 @@ def test_two_timescale_error_bound_independent_of_depth(alpha, beta):
         worst = max(worst, E.max() / (factor * emax))
     # the bound is not vacuous: the chain uses a sizeable part of it
     assert worst > 0.05
+
+
+@pytest.mark.parametrize("bits,ratio", [(4, 16 / 4.25), (8, 16 / 8.25)])
+def test_wire_bytes_per_pushed_element(bits, ratio):
+    """Abstract: sending 4-bit instead of 16-bit values cuts the all-reduce's
+    wire cost by nearly 4x.  Count the bytes the push actually writes for one
+    rank's non-owned segments (codes plus one binary16 scale and zero per
+    group of 128, found by writing over two different sentinels): 4.25 bits
+    per element at b = 4, so 16 / 4.25 = 3.76x fewer bytes than bf16."""
+    P, g = 4, 128
+    S = g * 16
+    n = P * S
+    xs = rand_partials(P, n, 41)
+    written = []
+    for fill in (0x00, 0xFF):
+        codes = np.full(oracle.code_bytes(n, bits), fill, np.uint8)
+        params = np.full(2 * (n // g), fill * 0x0101, np.uint16)
+        oracle.quantize_ef(xs[0], None, n, P, 0, 0, S, bits, g, codes, params, None)
+        written.append((codes.copy(), params.view(np.uint8).copy()))
+    (c0, p0), (c1, p1) = written
+    # a byte was written if it holds the same value after both sentinels
+    code_bytes = int(np.count_nonzero(c0 == c1))
+    param_bytes = int(np.count_nonzero(p0 == p1))
+    pushed = (P - 1) * S
+    assert code_bytes == pushed * bits // 8
+    assert param_bytes == pushed // g * 4
+    bits_per_elem = 8 * (code_bytes + param_bytes) / pushed
+    assert bits_per_elem == bits + 32 / g
+    assert abs(16 / bits_per_elem - ratio) < 1e-12
+    if bits == 4:
+        assert 3.5 < 16 / bits_per_elem < 4.0        # "nearly 4x"
