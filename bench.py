@@ -346,7 +346,7 @@ def main():
     a = ap.parse_args()
 
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (the P ranks are simulated on it); "
+        print(f"bench.py: the benchmark runs on one GPU only (the P ranks are simulated on it); "
               f"--gpus {a.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
