@@ -413,8 +413,8 @@ def test_two_timescale_error_bound_independent_of_depth(alpha, beta):
 
 @pytest.mark.parametrize("bits,ratio", [(4, 16 / 4.25), (8, 16 / 8.25)])
 def test_wire_bytes_per_pushed_element(bits, ratio):
-    """Abstract: sending 4-bit instead of 16-bit values cuts the all-reduce's
-    wire cost by nearly 4x.  Count the bytes the push actually writes for one
+    """Abstract: a 4-bit payload makes the all-reduce's traffic almost four
+    times smaller than a 16-bit one.  Count the bytes the push writes for one
     rank's non-owned segments (codes plus one binary16 scale and zero per
     group of 128, found by writing over two different sentinels): 4.25 bits
     per element at b = 4, so 16 / 4.25 = 3.76x fewer bytes than bf16."""
