@@ -23,6 +23,9 @@ Also printed (same JSON line):
                 summary if it was taken on the current kernel source.
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same
                 workload: 1/4 of every segment's groups, same byte formula.
+  cpu_baseline_threaded
+                the same sample as independent calls on ranges of every
+                segment, in up to 16 host threads.
   staged        the same call with tiles staggered across streams.
   variants      the same call with Table 8's ablation quantizers (naive zero
                 point, symmetric grid) and with groups of 256.
@@ -286,7 +289,8 @@ def device_copy_gbs(torch, reps=10):
 def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=4):
     """The oracle (single-threaded C) on a bounded sample of the workload:
     a message 1/frac_den the size (every segment shortened alike), drawn from
-    the same Laplace(0,1) recipe, timed over one whole call."""
+    the same Laplace(0,1) recipe, timed over one whole call; then the same
+    sample in host threads.  Returns (single-threaded, threaded)."""
     import numpy as np
     import oracle
     from error_feedback_quant_amd import inputs
@@ -297,15 +301,46 @@ def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=4):
     sample = [inputs.as_numpy_u16(inputs.laplace(r, P * L, device="cpu", chunk=1 << 24)) for r in range(P)]
     m = sample[0].size
     comps = [np.zeros(m, np.float32) for _ in range(P)] if ef else None
+    odt = oracle.OUT_BF16 if out_bf16 else oracle.OUT_F32
     t0 = time.perf_counter()
-    oracle.allreduce(sample, bits=bits, ef=ef, comps=comps,
-                     out_dtype=oracle.OUT_BF16 if out_bf16 else oracle.OUT_F32)
+    oracle.allreduce(sample, bits=bits, ef=ef, comps=comps, out_dtype=odt)
     dt = time.perf_counter() - t0
     B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4)
-    return {"value": round(P * m * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one call on {m} of {n} elements per rank (1/{frac_den} of every segment, "
-                      f"same distribution), P={P}, {dt:.2f} s single-threaded",
-            "cpu": host_cpu_model()}
+    single = {"value": round(P * m * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "sample": f"one call on {m} of {n} elements per rank (1/{frac_den} of every segment, "
+                        f"same distribution), P={P}, {dt:.2f} s single-threaded",
+              "cpu": host_cpu_model()}
+    # the same call as independent calls on mini messages made of the same
+    # range of every segment (groups and elements are independent), one per
+    # worker thread at a time; the oracle's C entry point releases the GIL
+    from concurrent.futures import ThreadPoolExecutor
+    workers = host_threads()
+    chunk = max(G, (L // (8 * workers)) // G * G)
+    comps = [np.zeros(m, np.float32) for _ in range(P)] if ef else None
+
+    def one(a0):
+        b0 = min(L, a0 + chunk)
+        xm = [np.concatenate([x[s * L + a0:s * L + b0] for s in range(P)]) for x in sample]
+        cm = [np.concatenate([c[s * L + a0:s * L + b0] for s in range(P)]) for c in comps] if ef else None
+        oracle.allreduce(xm, bits=bits, ef=ef, comps=cm, out_dtype=odt)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(one, range(0, L, chunk)))
+    dtt = time.perf_counter() - t0
+    threaded = {"value": round(P * m * B / dtt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+                "sample": f"the same sample as {-(-L // chunk)} independent calls on ranges of {chunk} elements "
+                          f"of every segment, {workers} threads, {dtt:.2f} s"}
+    return single, threaded
+
+
+def host_threads(cap: int = 16) -> int:
+    """Worker threads for the threaded oracle: the CPUs this process may run
+    on, at most `cap`."""
+    try:
+        return max(1, min(cap, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(cap, os.cpu_count() or 1))
 
 
 def host_cpu_model() -> str:
@@ -408,9 +443,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cpu = None
+    cpu = cpu_threaded = None
     if not a.no_cpu:
-        cpu = cpu_baseline(a.P, N_1GIB, a.bits, out_bf16, ef)
+        cpu, cpu_threaded = cpu_baseline(a.P, N_1GIB, a.bits, out_bf16, ef)
 
     line = {
         "metric": METRIC,
@@ -438,6 +473,7 @@ def main():
         },
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
+        "cpu_baseline_threaded": cpu_threaded,
         "staged": staged,
         "variants": variants,
         "modes": modes,
