@@ -5,7 +5,7 @@ with the compensation added in the entry pass, owner reduce, tail decode, and
 the compensator update (classic error feedback: -e written in place).  The
 headline schedule runs the stages back to back on one stream (one tile per
 segment), the fastest schedule on a single GPU; the same call with each
-segment split into 8 tiles staggered across 4 HIP streams is reported beside
+segment split into 4 tiles staggered across 4 HIP streams is reported beside
 it ("staged").  Inputs: 2^29 bfloat16 elements per rank, Laplace(0, 1),
 resident in HBM before timing starts.
 
@@ -364,7 +364,7 @@ def main():
     ap.add_argument("--bits", type=int, default=4, choices=[4, 8])
     ap.add_argument("--tiles", type=int, default=1)
     ap.add_argument("--streams", type=int, default=1)
-    ap.add_argument("--staged-tiles", type=int, default=8)
+    ap.add_argument("--staged-tiles", type=int, default=4)
     ap.add_argument("--staged-streams", type=int, default=4)
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-schedule leg")
     ap.add_argument("--no-variants", action="store_true",
