@@ -463,6 +463,9 @@ def main():
         "config": {
             "workload": f"1 GiB message: 2^29 bf16 elements per rank, Laplace(0,1), P={a.P} simulated ranks",
             "P": a.P, "bits": a.bits, "group": G, "tiles": a.tiles, "streams": a.streams,
+            "schedule": ("push, reduce and tail back to back on one stream, the fastest on one GPU; "
+                         "the tile-staged multi-stream schedule is reported under 'staged'")
+                        if (a.tiles, a.streams) == (1, 1) else "tile-staged across streams",
             "ef": "classic error feedback (alpha=1), -e written in place" if ef else "off",
             "out": a.out, "bytes_per_elem_per_rank": round(main_res["B"], 5),
             "bytes_per_call": int(main_res["bytes_per_call"]),
