@@ -41,8 +41,10 @@
  *    message-shaped: n*bits/8 bytes, segment s at byte offset s*S*bits/8.
  *  - Per-group parameters: one echo_qparam per group of `group` consecutive
  *    message elements (n/group entries, message-shaped): IEEE binary16 scale s
- *    and binary16 zero point z (an integer).  Decoding is v = (q - z) * s,
- *    exact in fp32.
+ *    and binary16 zero point z.  Decoding is v = (q - z) * s in fp32: exact
+ *    when z is an integer (the zero-aware quantizer and the symmetric-grid
+ *    ablation); the naive-zero-point ablation's z carries a fraction, so
+ *    there q - z may round.
  *  - Non-finite inputs give unspecified (but memory-safe) results.
  *  - Thread safety: calls are reentrant.  Calls that write the same buffers
  *    must be ordered by the caller.
@@ -61,7 +63,7 @@ enum echo_status {
     ECHO_OK = 0,
     ECHO_EINVAL = -1, /* null required pointer, bad P/rank/owner/constants */
     ECHO_EALIGN = -2, /* a data pointer is not 16-byte aligned */
-    ECHO_EUNSUP = -3, /* bits not 4/8, group not 128, unknown output dtype */
+    ECHO_EUNSUP = -3, /* bits not 4/8, group not 128/256, unknown output dtype */
     ECHO_ESHAPE = -4, /* n or tile not a valid multiple / out of range */
     ECHO_EHIP = -5    /* a HIP launch or runtime call failed; see echo_last_hip_error */
 };
@@ -81,7 +83,8 @@ enum {
 
 typedef struct echo_qparam {
     uint16_t scale_f16; /* binary16 bits of s */
-    uint16_t zero_f16;  /* binary16 bits of the integer zero point z */
+    uint16_t zero_f16;  /* binary16 bits of the zero point z (an integer except
+                           for the naive-zero-point ablation) */
 } echo_qparam;
 
 /*
