@@ -45,3 +45,15 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baselines_report_the_contract_fields():
+    """Both oracle baselines (single-threaded, and the same sample in host
+    threads) carry value, unit, cores, kind and a sample description, on a
+    small message here."""
+    single, threaded = bench.cpu_baseline(4, 4 * 128 * 256, 4, True, True)
+    for d in (single, threaded):
+        assert set(("value", "unit", "cores", "kind", "sample")) <= set(d)
+        assert d["unit"] == "GB/s" and d["kind"] == "oracle" and d["value"] > 0
+    assert single["cores"] == 1 and "cpu" in single
+    assert 1 <= threaded["cores"] <= 16
