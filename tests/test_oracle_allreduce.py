@@ -439,4 +439,4 @@ def test_wire_bytes_per_pushed_element(bits, ratio):
     assert bits_per_elem == bits + 32 / g
     assert abs(16 / bits_per_elem - ratio) < 1e-12
     if bits == 4:
-        assert 3.5 < 16 / bits_per_elem < 4.0        # "nearly 4x"
+        assert 3.5 < 16 / bits_per_elem < 4.0        # almost four times fewer bytes
