@@ -2,8 +2,8 @@
 
 The partial sums x = bf16(A W^T) of a row-parallel layer are the message of
 the all-reduce (Echo paper card Fig. 2(a)); the fused call is that matmul
-followed by the push step (article "The cancellation rule": the compensator
-is folded into the entry pass without changing the computed values).
+followed by the push step (article "The cancellation rule": folding the
+compensator into the entry pass leaves the results as they were).
 
 Pins: exact integer dot products (pure Python) with W in [N, K] layout, so a
 transposed operand or a swapped index fails; the bf16 rounding of a sum
