@@ -204,7 +204,7 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  * and push quantization fused into its epilogue.  Paper card Fig. 2(a) (each
  * rank quantizes its partial sums for the segments owned by other ranks);
  * article "The cancellation rule" (the compensator is folded into the entry
- * pass, beside the matmul, without changing the computed values).
+ * pass, beside the matmul, and the results stay as they were).
  *
  * Computes this rank's partial sums x = bf16(A W^T), i.e.
  *   x[m*N + j] = bfloat16(sum_k A[m][k] * W[j][k])   (fp32 accumulation,
