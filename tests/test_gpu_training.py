@@ -5,7 +5,7 @@ calls, with the two-timescale compensator (alpha = 0.5, beta = 0.25) fused
 into the kernels; each pass keeps its own compensation and slow memory,
 carried across steps (Echo paper card Fig. 1: the backward pass adds its
 errors at the forward pass's sites; PhantomByte article, "The cancellation rule": each error
-returns at the calls that follow).
+is paid back in later calls).
 
 Every call is checked bit for bit against the oracle on a row slice that
 keeps segment ownership (the first row of every segment: an exact

@@ -311,8 +311,8 @@ def test_depth_chain_two_timescale(echo):
     compensator (alpha = 0.5, beta = 0.25) fused into push and reduce: the
     accumulated error equals the outstanding debt sum_j (M_j - c_j) at every
     site and stays within twice the largest injected error, independent of
-    depth (PhantomByte article, "The cancellation rule": each error returns
-    at the calls that follow)."""
+    depth (PhantomByte article, "The cancellation rule": each error is paid
+    back in later calls)."""
     P, n, sites, bits, gen = chain_gen("chain")
     say("chain two-timescale")
     E, d, gap = chain_run(echo, P, n, sites, bits, gen, "two_timescale", alpha=0.5, beta=0.25)
