@@ -513,9 +513,9 @@ int echo_ref_gather_dequant(const uint8_t* sum_codes, const uint16_t* sum_params
 
 /* ------------------------------------------------------------------------ */
 /* O5: the two-timescale compensator update.                                 */
-/* [EchoCard] abstract (an error, once revealed, is returned in later      */
+/* [EchoCard] abstract (an error, once revealed, is returned in later        */
 /* calls and cancels); [Blog] "The cancellation rule" (a two-timescale       */
-/* compensator; each error is paid back in later calls).                    */
+/* compensator; each error is paid back in later calls).                     */
 /* The pages give no equation; the reading is an error debt with a fast      */
 /* fraction alpha and a slow memory M released at rate beta:                 */
 /*   c' = -(alpha*e + beta*M)          (the next call's compensation)        */
