@@ -24,6 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import threading
 from ctypes import POINTER, c_float, c_int, c_int64, c_uint16, c_void_p
 
 import numpy as np
@@ -44,20 +45,30 @@ CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fexcess-pr
 
 
 def build(force: bool = True) -> str:
-    """Compile echo_ref.c into libecho_ref.so with gcc (no GPU involved)."""
+    """Compile echo_ref.c into libecho_ref.so with gcc (no GPU involved).
+    The compiler writes a temporary file private to this process and thread,
+    which then replaces the library in one rename."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + ".tmp"
+        tmp = f"{LIB}.tmp{os.getpid()}.{threading.get_ident()}"
         subprocess.run(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, LIB)
     return LIB
 
 
 _lib = None
+_lib_lock = threading.Lock()
 
 
 def lib():
+    """The loaded oracle library, built first if missing or older than its
+    source.  Safe to call from several threads at once (the chunked oracle
+    runs its calls in a thread pool)."""
     global _lib
-    if _lib is None:
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
         if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
             build(force=True)
         L = ctypes.CDLL(LIB)

@@ -174,6 +174,63 @@ def test_onegb_full_parity(echo, P):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("mode", ["ef_off", "f32_out", "two_timescale", "bits8"])
+def test_onegb_full_parity_modes(echo, mode):
+    """The benchmark's other legs at full size (1 GiB message, P = 4, one tile
+    on one stream): feedback off, fp32 output, the two-timescale compensator
+    (alpha = 0.5, beta = 0.25) fused into push and reduce, and 8-bit codes.
+    Two calls carry the state; every output, compensation and slow-memory
+    element matches the oracle's whole call bit for bit."""
+    P, n = 4, 1 << 29
+    L = 1 << 18
+    ef = mode != "ef_off"
+    two = mode == "two_timescale"
+    bits = 8 if mode == "bits8" else 4
+    odt = oracle.OUT_F32 if mode == "f32_out" else oracle.OUT_BF16
+    alpha, beta = (0.5, 0.25) if two else (1.0, 0.0)
+    workers = host_workers()
+    torch.cuda.empty_cache()
+    comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if ef else None
+    slows = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if two else None
+    outs = [torch.empty(n, dtype=torch.float32 if odt == oracle.OUT_F32 else torch.int16, device=DEV)
+            for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
+    c_host = [np.zeros(n, np.float32) for _ in range(P)] if ef else None
+    s_host = [np.zeros(n, np.float32) for _ in range(P)] if two else None
+    for call in range(2):
+        say("onegb mode", mode, "call", call)
+        xs = [inputs.laplace(r + 16 * call, n, device=DEV) for r in range(P)]
+        xh = [host_u16(x) for x in xs]
+        a = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=1, out_dtype=odt, ef=ef, alpha=alpha, beta=beta,
+                               comps=comps, slows=slows)
+        echo.echo_allreduce_sim(a)
+        torch.cuda.synchronize()
+        out_h = [host_f32(o) if odt == oracle.OUT_F32 else host_u16(o) for o in outs]
+        c_after = [host_f32(c) for c in comps] if ef else None
+        s_after = [host_f32(m) for m in slows] if two else None
+        del xs
+
+        def visit(sl, o_outs, o_c, o_s):
+            for r in range(P):
+                if gather_chunk(out_h[r], sl).tobytes() != o_outs[r].tobytes():
+                    return f"{mode} call {call}: out[{r}] differs in the range at {sl[0].start} of segment 0"
+                if ef and gather_chunk(c_after[r], sl).tobytes() != o_c[r].tobytes():
+                    return f"{mode} call {call}: comp[{r}] differs in the range at {sl[0].start} of segment 0"
+                if two and gather_chunk(s_after[r], sl).tobytes() != o_s[r].tobytes():
+                    return f"{mode} call {call}: slow[{r}] differs in the range at {sl[0].start} of segment 0"
+            return None
+
+        t0 = time.time()
+        bad = oracle_by_chunks(xh, c_host, P, L, odt, workers, visit, bits=bits, slows=s_host, alpha=alpha,
+                               beta=beta)
+        print(f"onegb mode {mode} call {call}: oracle and compare {time.time() - t0:.1f} s", flush=True)
+        assert bad is None, bad
+        del xh, out_h
+        c_host, s_host = c_after, s_after
+    del comps, slows, outs, ws
+    torch.cuda.empty_cache()
+
+
 def test_message_beyond_2_31_elements(echo):
     """2^31 + 2^22 elements per rank (P = 2, about 38 GB on the device):
     every element of segment 1 lies beyond 2^31, so do its fp32 byte offsets
