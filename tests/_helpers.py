@@ -89,7 +89,7 @@ def gather_chunk(arr: np.ndarray, sl) -> np.ndarray:
 
 
 def oracle_by_chunks(xs, comps, P, L, out_dtype, workers, visit, bits=4, slows=None, alpha=1.0,
-                     beta=0.0):
+                     beta=0.0, quant="zero_aware", group=128):
     """The oracle's whole call over a message of P segments, computed as
     independent calls on mini messages made of the same L-element range of
     every segment.  Feedback is on when `comps` is given (classic, written
@@ -106,15 +106,15 @@ def oracle_by_chunks(xs, comps, P, L, out_dtype, workers, visit, bits=4, slows=N
 
     n = xs[0].size
     S = n // P
-    assert S % L == 0 and L % 128 == 0
+    assert S % L == 0 and L % group == 0
 
     def one(a):
         sl = chunk_slices(P, S, a, a + L)
         xm = [gather_chunk(x, sl) for x in xs]
         cm = [gather_chunk(c, sl) for c in comps] if comps is not None else None
         sm = [gather_chunk(m, sl) for m in slows] if slows is not None else None
-        outs, _, _ = oracle.allreduce(xm, bits=bits, ef=comps is not None, alpha=alpha, beta=beta,
-                                      comps=cm, slows=sm, out_dtype=out_dtype)
+        outs, _, _ = oracle.allreduce(xm, bits=bits, group=group, ef=comps is not None, alpha=alpha, beta=beta,
+                                      comps=cm, slows=sm, out_dtype=out_dtype, quant=quant)
         return visit(sl, outs, cm, sm)
 
     with ThreadPoolExecutor(max_workers=workers) as pool:

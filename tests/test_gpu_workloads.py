@@ -174,18 +174,21 @@ def test_onegb_full_parity(echo, P):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("mode", ["ef_off", "f32_out", "two_timescale", "bits8"])
+@pytest.mark.parametrize("mode", ["ef_off", "f32_out", "two_timescale", "bits8", "naive", "symmetric", "g256"])
 def test_onegb_full_parity_modes(echo, mode):
     """The benchmark's other legs at full size (1 GiB message, P = 4, one tile
     on one stream): feedback off, fp32 output, the two-timescale compensator
-    (alpha = 0.5, beta = 0.25) fused into push and reduce, and 8-bit codes.
-    Two calls carry the state; every output, compensation and slow-memory
-    element matches the oracle's whole call bit for bit."""
+    (alpha = 0.5, beta = 0.25) fused into push and reduce, 8-bit codes, and
+    Table 8's naive-zero-point and symmetric-grid quantizers and groups of
+    256.  Two calls carry the state; every output, compensation and
+    slow-memory element matches the oracle's whole call bit for bit."""
     P, n = 4, 1 << 29
     L = 1 << 18
     ef = mode != "ef_off"
     two = mode == "two_timescale"
     bits = 8 if mode == "bits8" else 4
+    quant = mode if mode in ("naive", "symmetric") else "zero_aware"
+    group = 256 if mode == "g256" else 128
     odt = oracle.OUT_F32 if mode == "f32_out" else oracle.OUT_BF16
     alpha, beta = (0.5, 0.25) if two else (1.0, 0.0)
     workers = host_workers()
@@ -194,15 +197,15 @@ def test_onegb_full_parity_modes(echo, mode):
     slows = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)] if two else None
     outs = [torch.empty(n, dtype=torch.float32 if odt == oracle.OUT_F32 else torch.int16, device=DEV)
             for _ in range(P)]
-    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits, group), dtype=torch.uint8, device=DEV)
     c_host = [np.zeros(n, np.float32) for _ in range(P)] if ef else None
     s_host = [np.zeros(n, np.float32) for _ in range(P)] if two else None
     for call in range(2):
         say("onegb mode", mode, "call", call)
         xs = [inputs.laplace(r + 16 * call, n, device=DEV) for r in range(P)]
         xh = [host_u16(x) for x in xs]
-        a = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=1, out_dtype=odt, ef=ef, alpha=alpha, beta=beta,
-                               comps=comps, slows=slows)
+        a = echo.make_sim_args(xs, outs, ws, bits=bits, group=group, tiles=1, out_dtype=odt, ef=ef, alpha=alpha,
+                               beta=beta, comps=comps, slows=slows, quant=quant)
         echo.echo_allreduce_sim(a)
         torch.cuda.synchronize()
         out_h = [host_f32(o) if odt == oracle.OUT_F32 else host_u16(o) for o in outs]
@@ -222,7 +225,7 @@ def test_onegb_full_parity_modes(echo, mode):
 
         t0 = time.time()
         bad = oracle_by_chunks(xh, c_host, P, L, odt, workers, visit, bits=bits, slows=s_host, alpha=alpha,
-                               beta=beta)
+                               beta=beta, quant=quant, group=group)
         print(f"onegb mode {mode} call {call}: oracle and compare {time.time() - t0:.1f} s", flush=True)
         assert bad is None, bad
         del xh, out_h

@@ -440,3 +440,33 @@ def test_wire_bytes_per_pushed_element(bits, ratio):
     assert abs(16 / bits_per_elem - ratio) < 1e-12
     if bits == 4:
         assert 3.5 < 16 / bits_per_elem < 4.0        # almost four times fewer bytes
+
+
+@pytest.mark.parametrize("quant,group", [("naive", 128), ("symmetric", 128), ("zero_aware", 256)])
+def test_chunked_calls_equal_one_whole_call_variants(quant, group):
+    """The chunked form of the oracle's call (as the full-size GPU parity runs
+    it) for Table 8's quantizers and groups of 256: equal to one whole call,
+    bit for bit."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from _helpers import oracle_by_chunks, gather_chunk
+
+    P, S = 4, 256 * 12
+    n = P * S
+    rng = np.random.default_rng(11)
+    xs = [oracle.f32_to_bf16_bits(rng.laplace(size=n).astype(np.float32)) for _ in range(P)]
+    comps0 = [(rng.standard_normal(n) * 0.05).astype(np.float32) for _ in range(P)]
+    whole_c = [c.copy() for c in comps0]
+    whole, _, _ = oracle.allreduce(xs, bits=4, group=group, ef=True, comps=whole_c, out_dtype=oracle.OUT_BF16,
+                                   quant=quant)
+
+    def visit(sl, outs, cm, sm):
+        for r in range(P):
+            if gather_chunk(whole[r], sl).tobytes() != outs[r].tobytes():
+                return f"out[{r}] at {sl[0].start}"
+            if gather_chunk(whole_c[r], sl).tobytes() != cm[r].tobytes():
+                return f"comp[{r}] at {sl[0].start}"
+        return None
+
+    for L in (256, 256 * 4):
+        assert oracle_by_chunks(xs, comps0, P, L, oracle.OUT_BF16, 4, visit, quant=quant, group=group) is None
