@@ -40,6 +40,9 @@ constexpr int kUPush = ECHO_U_PUSH;
 constexpr int kURed = ECHO_U_RED;
 constexpr int kUGath = ECHO_U_GATH;
 constexpr size_t kReduceCompLds = 32 * 1024;
+// tiles per segment in one simulated call: results do not depend on the
+// tiling, and each tile takes two events from the pool
+constexpr int64_t kMaxTiles = 4096;
 
 int hip_fail(hipError_t e)
 {
@@ -488,6 +491,7 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
     const int64_t groups_per_seg = S / a->group;
     int64_t T = a->tiles;
     if (T > groups_per_seg) T = groups_per_seg;
+    if (T > kMaxTiles) T = kMaxTiles;   // bounds the events this call needs
     const int64_t tile_groups = (groups_per_seg + T - 1) / T;
     const int64_t tile_len = tile_groups * a->group;
     T = (S + tile_len - 1) / tile_len;

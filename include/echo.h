@@ -271,7 +271,7 @@ typedef struct echo_sim_args {
     int P;          /* ranks, 1..8 */
     int bits;       /* 4 or 8 */
     int group;      /* 128 or 256 */
-    int tiles;      /* tiles per segment, >= 1 (capped at S/group) */
+    int tiles;      /* tiles per segment, >= 1 (capped at S/group and at 4096) */
     int out_dtype;  /* ECHO_OUT_F32 or ECHO_OUT_BF16 */
     int ef;         /* 0: no compensation; 1: compensation on */
     int quant;      /* 0 (zero-aware), ECHO_QUANT_NAIVE or ECHO_QUANT_SYMMETRIC */

@@ -157,6 +157,21 @@ def test_staged_equals_serial(echo, bits):
             assert_bits_equal(gstate["comps"][r], rstate["comps"][r], f"comp {r}")
 
 
+def test_tile_count_is_capped(echo):
+    """A tile count far above the cap (4096 per segment) on a message with
+    more groups per segment than that: same bits as one tile, two calls."""
+    P, n = 2, 2 * G * 4200
+    xs_list = [[rand_bf16(n, 500 + 10 * c + r) for r in range(P)] for c in range(2)]
+    say("tile cap", n)
+    ref, rstate = run_gpu_calls(echo, xs_list, P, n, 4, "classic", oracle.OUT_BF16, 1, 1)
+    got, gstate = run_gpu_calls(echo, xs_list, P, n, 4, "classic", oracle.OUT_BF16, 100000, 3)
+    for c in range(2):
+        for r in range(P):
+            assert_bits_equal(got[c][r], ref[c][r], f"capped tiles call {c} rank {r}")
+    for r in range(P):
+        assert_bits_equal(gstate["comps"][r], rstate["comps"][r], f"comp {r}")
+
+
 def test_sim_empty_message_is_a_no_op(echo):
     say("empty")
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
