@@ -382,3 +382,29 @@ def test_depth_chain_two_timescale(echo):
     assert E.max() <= 2.0 * d.max()
     # the bound does not grow with depth: the second half is no worse than 1.1x the first
     assert E[sites // 2:].max() <= 1.1 * E[:sites // 2].max()
+
+
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, 0.25)])
+def test_compensate_full_size(echo, alpha, beta):
+    """echo_compensate on 2^29 + 3 elements (the state of one rank at the
+    1 GiB message, plus a ragged remainder): the grid-stride loop runs many
+    rounds per thread at this size.  The new compensation and slow memory
+    match the oracle's update bit for bit."""
+    n = (1 << 29) + 3
+    say("compensate full size", alpha, beta, n)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(20261202 + int(alpha * 1000) + int(beta * 100))
+    e_d = torch.randn(n, generator=g, device=DEV) * 0.01
+    c_d = torch.full((n,), 9.0, device=DEV)
+    m_d = torch.randn(n, generator=g, device=DEV) * 0.02 if beta > 0 else None
+    e = host_f32(e_d)
+    c = np.full(n, 9.0, np.float32)
+    m = host_f32(m_d).copy() if m_d is not None else None
+    echo.echo_compensate(e_d, c_d, m_d, n, alpha, beta)
+    torch.cuda.synchronize()
+    oracle.compensate(e, c, m, n, alpha, beta)
+    assert_bits_equal(host_f32(c_d), c, "comp")
+    if m is not None:
+        assert_bits_equal(host_f32(m_d), m, "slow")
+    del e_d, c_d, m_d
+    torch.cuda.empty_cache()
