@@ -408,3 +408,33 @@ def test_compensate_full_size(echo, alpha, beta):
         assert_bits_equal(host_f32(m_d), m, "slow")
     del e_d, c_d, m_d
     torch.cuda.empty_cache()
+
+
+def test_maximum_message_size(echo):
+    """The largest message the library accepts: 2^34 elements per rank
+    (P = 2, feedback off, bf16 output; about 155 GB of device memory).  Every
+    offset of segment 1 lies beyond 2^33 elements.  Sampled groups at both
+    ends and inside both segments match the oracle bit for bit, the two
+    ranks' outputs agree over the whole message, and a message one group
+    pair longer is rejected."""
+    P = 2
+    n = 1 << 34
+    S = n // P
+    torch.cuda.empty_cache()
+    say("maximum size", n, "generate")
+    xs = [inputs.laplace(r + 60, n, device=DEV) for r in range(P)]
+    outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, 4), dtype=torch.uint8, device=DEV)
+    idx = sample_index(P, S, 24, seed=34)
+    x_mini = [host_u16(x[idx]) for x in xs]
+    say("maximum size", n, "call")
+    a = echo.make_sim_args(xs, outs, ws, bits=4, tiles=1, out_dtype=oracle.OUT_BF16, ef=False)
+    echo.echo_allreduce_sim(a)
+    torch.cuda.synchronize()
+    o_outs, _, _ = oracle.allreduce(x_mini, bits=4, ef=False, out_dtype=oracle.OUT_BF16)
+    for r in range(P):
+        assert_bits_equal(host_u16(outs[r][idx]), o_outs[r], f"out[{r}] sample")
+    assert torch.equal(outs[1], outs[0]), "the ranks differ"
+    assert echo.echo_allreduce_sim_workspace_bytes(P, n + 2 * G, 4) == 0   # beyond the limit
+    del xs, outs, ws
+    torch.cuda.empty_cache()
