@@ -421,6 +421,10 @@ def test_maximum_message_size(echo):
     n = 1 << 34
     S = n // P
     torch.cuda.empty_cache()
+    need = P * n * 2 * 2 + echo.echo_allreduce_sim_workspace_bytes(P, n, 4) + (4 << 30)
+    free, _ = torch.cuda.mem_get_info()
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
     say("maximum size", n, "generate")
     xs = [inputs.laplace(r + 60, n, device=DEV) for r in range(P)]
     outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
