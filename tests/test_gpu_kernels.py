@@ -215,6 +215,13 @@ def edge_groups(bits):
     gs.append(np.resize(np.array([0.0, Qm * mid, 3.0, 7.25]), G))
     gs.append(np.resize(np.array([0.0, Qm * (1.0 + 3 * 2.0 ** -11)]), G))  # the other tie direction
     gs.append(np.full(G, 3.0))                               # constant nonzero group
+    # exact ties with an odd integer zero point (z = 3: the zero point must be
+    # added after rounding), and zero-point ties at 2.5 (-> 2) and 3.5 (-> 4)
+    for z2 in (6, 5, 7):                                     # -lo/s = z2 / 2
+        lo = -0.5 * z2 * s; hi = lo + Qm * s
+        t = np.concatenate([[lo, hi], (np.arange(-z2, 2 * Qm - z2) * 0.5) * s])
+        gs.append(np.resize(t, G))
+    gs.append(np.resize(np.array([-3 * s, (Qm - 3) * s, 0.5 * s, 1.5 * s, -0.5 * s, 2.5 * s, -2.5 * s]), G))
     return [g.astype(np.float32) for g in gs]
 
 
