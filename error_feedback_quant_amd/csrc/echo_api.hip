@@ -27,18 +27,9 @@ thread_local int t_last_hip_error = 0;
 constexpr int64_t kMaxN = int64_t(1) << 34;
 // passes of 16 groups per block (each DPP row handles this many groups),
 // per kernel; chosen by measurement at the 1 GiB workload
-#ifndef ECHO_U_PUSH
-#define ECHO_U_PUSH 2
-#endif
-#ifndef ECHO_U_RED
-#define ECHO_U_RED 2
-#endif
-#ifndef ECHO_U_GATH
-#define ECHO_U_GATH 2
-#endif
-constexpr int kUPush = ECHO_U_PUSH;
-constexpr int kURed = ECHO_U_RED;
-constexpr int kUGath = ECHO_U_GATH;
+constexpr int kUPush = 2;
+constexpr int kURed = 2;
+constexpr int kUGath = 2;
 constexpr size_t kReduceCompLds = 32 * 1024;
 // tiles per segment in one simulated call: results do not depend on the
 // tiling, and each tile takes two events from the pool

@@ -56,45 +56,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------- helpers --
 
 // Streaming accesses: every byte of the message is touched once per kernel,
-// so loads and stores of the big arrays may carry the non-temporal hint.
-#ifndef ECHO_NT
-#define ECHO_NT 1
-#endif
-#ifndef ECHO_NT_LD
-#define ECHO_NT_LD ECHO_NT
-#endif
-#ifndef ECHO_NT_ST
-#define ECHO_NT_ST ECHO_NT
-#endif
+// so loads and stores of the big arrays carry the non-temporal hint (measured
+// faster than plain accesses on both sides).
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p)
 {
-    if constexpr (ECHO_NT_LD) return __builtin_nontemporal_load(p);
-    else return *p;
+    return __builtin_nontemporal_load(p);
 }
 template <typename T>
 __device__ __forceinline__ void st_stream(T* p, const T& v)
 {
-    if constexpr (ECHO_NT_ST) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
-// the tail's decoded output (write-only stream)
-#ifndef ECHO_NT_OUT
-#define ECHO_NT_OUT 1
-#endif
-template <typename T>
-__device__ __forceinline__ void st_out(T* p, const T& v)
-{
-    if constexpr (ECHO_NT_OUT) __builtin_nontemporal_store(v, p);
-    else *p = v;
+    __builtin_nontemporal_store(v, p);
 }
 
 // fp32 streams (compensation in, error out) go through a wave-private LDS
 // slice so that every global fp32 access is lane-contiguous (1 KB per wave
 // instruction) while the arithmetic keeps 8 consecutive elements per lane.
-#ifndef ECHO_STAGE
-#define ECHO_STAGE 1
-#endif
 constexpr int kWaveChunk = 4 * kRow;   // 512 elements: the 4 rows of one wave
 
 // orders this wave's LDS accesses across lanes (no block barrier needed: the
@@ -476,7 +453,7 @@ template <int U, bool UPD>
 struct Fp32Io {
     static constexpr int kSlices = UPD ? 2 : 1;
     static constexpr int kPassStride = (kBlock / 64) * kWaveChunk;       // floats per pass (4 waves)
-    static constexpr int kLdsFloats = ECHO_STAGE ? U * kSlices * kPassStride : 1;
+    static constexpr int kLdsFloats = U * kSlices * kPassStride;
 
     f32x4 c0[U], c1[U], m0[U], m1[U];
 
@@ -485,29 +462,18 @@ struct Fp32Io {
         return lds + (k * kSlices + which) * kPassStride + wave * kWaveChunk;
     }
 
-    __device__ __forceinline__ void load(int k, const WaveMap& wm, int64_t e0, const float* comp,
-                                         const float* slow)
+    __device__ __forceinline__ void load(int k, const WaveMap& wm, const float* comp, const float* slow)
     {
-        if (ECHO_STAGE) {
-            c0[k] = ld_stream((const f32x4*)(comp + wm.contig(0)));
-            c1[k] = ld_stream((const f32x4*)(comp + wm.contig(1)));
-            if (UPD) {
-                m0[k] = ld_stream((const f32x4*)(slow + wm.contig(0)));
-                m1[k] = ld_stream((const f32x4*)(slow + wm.contig(1)));
-            }
-        } else {
-            c0[k] = ld_stream((const f32x4*)(comp + e0));
-            c1[k] = ld_stream((const f32x4*)(comp + e0 + 4));
-            if (UPD) {
-                m0[k] = ld_stream((const f32x4*)(slow + e0));
-                m1[k] = ld_stream((const f32x4*)(slow + e0 + 4));
-            }
+        c0[k] = ld_stream((const f32x4*)(comp + wm.contig(0)));
+        c1[k] = ld_stream((const f32x4*)(comp + wm.contig(1)));
+        if (UPD) {
+            m0[k] = ld_stream((const f32x4*)(slow + wm.contig(0)));
+            m1[k] = ld_stream((const f32x4*)(slow + wm.contig(1)));
         }
     }
 
     __device__ __forceinline__ void stage(float* lds, uint32_t wave, uint32_t lane)
     {
-        if (!ECHO_STAGE) return;
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             stage_in(slice(lds, k, 0, wave), lane, c0[k], c1[k]);
@@ -519,34 +485,19 @@ struct Fp32Io {
     // the lane's 8 natural values of pass k (which = 0: comp, 1: slow)
     __device__ __forceinline__ void natural(float* lds, int k, int which, uint32_t wave, uint32_t lane, float* v) const
     {
-        if (ECHO_STAGE) {
-            natural_read(slice(lds, k, which, wave), lane, v);
-        } else {
-            const f32x4& a = which ? m0[k] : c0[k];
-            const f32x4& b = which ? m1[k] : c1[k];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        }
+        natural_read(slice(lds, k, which, wave), lane, v);
     }
 
-    // stage the 8 natural outputs of pass k for slice `which`, or store them
-    // directly when not staging
-    __device__ __forceinline__ void put(float* lds, int k, int which, uint32_t wave, uint32_t lane,
-                                        const float* v, bool active, float* dst, int64_t e0)
+    // stage the 8 natural outputs of pass k for slice `which`
+    __device__ __forceinline__ void put(float* lds, int k, int which, uint32_t wave, uint32_t lane, const float* v)
     {
-        if (ECHO_STAGE) {
-            natural_write(slice(lds, k, which, wave), lane, v);
-        } else if (active) {
-            st_stream((f32x4*)(dst + e0), f32x4{v[0], v[1], v[2], v[3]});
-            st_stream((f32x4*)(dst + e0 + 4), f32x4{v[4], v[5], v[6], v[7]});
-        }
+        natural_write(slice(lds, k, which, wave), lane, v);
     }
 
     // after all passes: the staged outputs go out lane-contiguously
     __device__ __forceinline__ void flush(float* lds, uint32_t wave, uint32_t lane, const WaveMap* wm,
                                           float* dst0, float* dst1)
     {
-        if (!ECHO_STAGE) return;
         wave_lds_fence();
 #pragma unroll
         for (int k = 0; k < U; ++k) {
@@ -626,7 +577,7 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
         wm[k].lane = lane;
         const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
         xv[k] = ld_stream((const u32x4*)(a.x + e0));
-        if (has_comp) io.load(k, wm[k], e0, a.comp, a.upd.slow);
+        if (has_comp) io.load(k, wm[k], a.comp, a.upd.slow);
     }
     if (has_comp) io.stage(lds, wave, lane);
 #pragma unroll
@@ -650,11 +601,11 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
             io.natural(lds, k, 1, wave, lane, m);
 #pragma unroll
             for (int i = 0; i < 8; ++i) update1(a.upd, e[i], m[i], cn[i], mn[i]);
-            io.put(lds, k, 0, wave, lane, cn, active, (float*)a.comp, e0);
-            io.put(lds, k, 1, wave, lane, mn, active, a.upd.slow, e0);
+            io.put(lds, k, 0, wave, lane, cn);
+            io.put(lds, k, 1, wave, lane, mn);
         } else if (has_out) {
             group_error(q, p, u, a.negate != 0, e);
-            io.put(lds, k, 0, wave, lane, e, active, a.err, e0);
+            io.put(lds, k, 0, wave, lane, e);
         }
     }
     if (has_out) io.flush(lds, wave, lane, wm, UPD ? (float*)a.comp : a.err, a.upd.slow);
@@ -712,7 +663,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
         wm[k].lane = lane;
         const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
         xv[k] = ld_stream((const u32x4*)(a.x + e0));
-        if (has_comp) io.load(k, wm[k], e0, a.comp, a.upd.slow);
+        if (has_comp) io.load(k, wm[k], a.comp, a.upd.slow);
 #pragma unroll
         for (int j = 0; j < kMaxP; ++j) {
             if (j < a.P && j != a.owner) {
@@ -759,11 +710,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
             io.natural(lds, k, 1, wave, lane, m);
 #pragma unroll
             for (int i = 0; i < 8; ++i) update1(a.upd, e[i], m[i], cn[i], mn[i]);
-            io.put(lds, k, 0, wave, lane, cn, active, (float*)a.comp, e0);
-            io.put(lds, k, 1, wave, lane, mn, active, a.upd.slow, e0);
+            io.put(lds, k, 0, wave, lane, cn);
+            io.put(lds, k, 1, wave, lane, mn);
         } else if (has_out) {
             group_error(q, p, acc, a.negate != 0, e);
-            io.put(lds, k, 0, wave, lane, e, active, a.err, e0);
+            io.put(lds, k, 0, wave, lane, e);
         }
     }
     if (has_out) io.flush(lds, wave, lane, wm, UPD ? (float*)a.comp : a.err, a.upd.slow);
@@ -787,8 +738,7 @@ struct GatherArgs {
 template <int BITS, bool OUT_BF16, int U, int GROUP>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 {
-    constexpr bool kStageOut = !OUT_BF16 && ECHO_STAGE;
-    __shared__ float lds[kStageOut ? U * (kBlock / 64) * kWaveChunk : 1];
+    __shared__ float lds[OUT_BF16 ? 1 : U * (kBlock / 64) * kWaveChunk];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = threadIdx.x & 15u;
@@ -819,16 +769,12 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
             w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
             w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
             w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
-            st_out((u32x4*)((uint16_t*)a.out + e0), w);
-        } else if (kStageOut) {
-            natural_write(lds + (k * (kBlock / 64) + wave) * kWaveChunk, lane, v);
+            st_stream((u32x4*)((uint16_t*)a.out + e0), w);
         } else {
-            float* o = (float*)a.out + e0;
-            st_out((f32x4*)o, f32x4{v[0], v[1], v[2], v[3]});
-            st_out((f32x4*)(o + 4), f32x4{v[4], v[5], v[6], v[7]});
+            natural_write(lds + (k * (kBlock / 64) + wave) * kWaveChunk, lane, v);
         }
     }
-    if constexpr (kStageOut) {
+    if constexpr (!OUT_BF16) {
         // rows past the tile were not decoded and are not stored
         wave_lds_fence();
 #pragma unroll
@@ -842,7 +788,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 #pragma unroll
             for (uint32_t h = 0; h < 2; ++h) {
                 if (!wm.contig_active(h)) continue;
-                st_out((f32x4*)((float*)a.out + wm.contig(h)), *(const f32x4*)(sl + 256 * h + 4 * lane));
+                st_stream((f32x4*)((float*)a.out + wm.contig(h)), *(const f32x4*)(sl + 256 * h + 4 * lane));
             }
         }
     }
