@@ -3,11 +3,12 @@
 A step is one echo_allreduce_sim call over P simulated ranks: push quantize
 with the compensation added in the entry pass, owner reduce, tail decode, and
 the compensator update (classic error feedback: -e written in place).  The
-headline schedule runs the stages back to back on one stream (one tile per
-segment), the fastest schedule on a single GPU; the same call with each
-segment split into 4 tiles staggered across 4 HIP streams is reported beside
-it ("staged").  Inputs: 2^29 bfloat16 elements per rank, Laplace(0, 1),
-resident in HBM before timing starts.
+headline runs the tile-staged schedule: each segment is split into 4 tiles
+whose stages overlap on two HIP streams (the push of tile t + 1 beside the
+owner reduce of tile t, the tail of tile t after it), ordered by events.  The
+same call with the stages back to back on one stream (one tile) is reported
+beside it.  Inputs: 2^29 bfloat16 elements per rank, Laplace(0, 1), resident
+in HBM before timing starts.
 
 value = algorithmic bytes of the call / time, in GB/s (10^9 B/s), where the
 algorithmic bytes per message element per rank are
@@ -15,18 +16,30 @@ algorithmic bytes per message element per rank are
 (bf16 in, output o bytes, compensation read + write, codes and per-group
 parameters written by the push, read by the owner, written once by the
 owner, read by every rank's tail).  Each simulated rank does its own reads.
+elements/s counts the P*n elements the call all-reduces.
 
 Also printed (same JSON line):
-  roofline      the dominant kernel (push quantize): algorithmic bytes per
-                launch / its mean launch time from HIP events on its stream,
-                against 8 TB/s; traffic from the committed rocprofv3 counter
-                summary if it was taken on the current kernel source.
-  cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same
-                workload: 1/4 of every segment's groups, same byte formula.
-  cpu_baseline_threaded
-                the same sample as independent calls on ranges of every
-                segment, in up to 16 host threads.
-  staged        the same call with tiles staggered across streams.
+  roofline      the dominant kernel (push quantize of one rank over whole
+                segments, as the back-to-back schedule launches it):
+                algorithmic bytes per launch / its mean launch time from HIP
+                events on its stream, against 8 TB/s; traffic from the
+                committed rocprofv3 counter summary if it was taken on the
+                current kernel source.
+  serial        the same call with the stages back to back on one stream.
+  p8            the same measurement at P = 8 (staged and serial), with its
+                own roofline.
+  configs       per-call throughput of the other workloads: a single call of
+                64 x 1024 per rank (latency, cache-resident), the depth-chain
+                call (2048 x 4096, feedback on and off), the 8-bit chain call
+                (4096 x 1024, on and off) and the training call (2^27 per
+                rank, two-timescale compensator, fused and as a separate
+                update pass).
+  cpu_baseline  the CPU oracle (single thread) on 1/64 of every segment of
+                the 1 GiB message, scaled to the whole call.
+  cpu_baselines the rest of the oracle's timing plan: single-threaded calls
+                of the other workloads and of P = 8, and the whole 1 GiB call
+                as independent calls on ranges of every segment in host
+                threads, at P = 4 and 8; with the host's CPU count and model.
   variants      the same call with Table 8's ablation quantizers (naive zero
                 point, symmetric grid) and with groups of 256.
   modes         the same call with feedback off, with fp32 output, with
@@ -38,10 +51,6 @@ Also printed (same JSON line):
                 echo_quantize_ef, at the Llama-3-8B down projection (TP = 4),
                 with an MFMA roofline; and the two-timescale update run
                 beside the next matmul against back to back.
-  config        also carries the per-call median and minimum (HIP events
-                between consecutive calls) and a plain 1 GiB device copy's
-                bandwidth as a measured second denominator.
-  p8            the same measurement at P = 8.
 """
 from __future__ import annotations
 
@@ -59,6 +68,7 @@ HBM_PEAK_GBS = 8000.0
 G = 128
 N_1GIB = 1 << 29
 METRIC = "fused quant/reduce/gather GB/s and % of HBM peak per call, 1 GB msg, P=4/8"
+STAGED_TILES, STAGED_STREAMS = 4, 2
 
 
 def kernel_source_hash() -> str:
@@ -82,15 +92,16 @@ def push_bytes_per_elem(bits, ef):
     return 2 + (8 if ef else 0) + bits / 8 + 4 / G
 
 
-def committed_traffic(P, tiles, n):
-    """HBM traffic per push launch from profiles/push_quantize_onegb_counters.json,
-    if those counters were taken on the current kernel source and shape."""
+def committed_traffic(P, n):
+    """HBM traffic per push launch (whole segments) from
+    profiles/push_quantize_onegb_counters.json, if those counters were taken
+    on the current kernel source and shape."""
     path = os.path.join(ROOT, "profiles", "push_quantize_onegb_counters.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
-        key = f"P{P}_tiles{tiles}_n{n}"
+        key = f"P{P}_tiles1_n{n}"
         if d.get("kernel_source_hash") != kernel_source_hash() or key not in d.get("push", {}):
             return None
         return d["push"][key]["hbm_bytes_per_launch"]
@@ -98,13 +109,27 @@ def committed_traffic(P, tiles, n):
         return None
 
 
+def schedule_name(tiles, nstreams):
+    if (tiles, nstreams) == (1, 1):
+        return "push, reduce and tail back to back on one stream (one tile per segment)"
+    if nstreams == 2:
+        return (f"{tiles} tiles per segment staged across 2 HIP streams: the push of tile t+1 runs beside "
+                f"the owner reduce of tile t, the tail of tile t follows on the push stream; events order each tile")
+    return f"{tiles} tiles per segment staged across {nstreams} HIP streams (push, reduce, tail on their own)"
+
+
 def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, out_bf16, ef, time_kernel=True,
-             quant="zero_aware", group=G, alpha=1.0, beta=0.0):
+             quant="zero_aware", group=G, alpha=1.0, beta=0.0, xs=None, unfused=False):
+    """Time `steps` calls of echo_allreduce_sim.  xs: the ranks' bf16 inputs
+    on the device (default: the 1 GiB Laplace workload's draw).  unfused:
+    errors go to err buffers and echo_compensate runs as its own pass."""
     dev = "cuda:0"
     two = ef and (alpha != 1.0 or beta != 0.0)
-    xs = [inputs.laplace(r, n, device=dev) for r in range(P)]
+    if xs is None:
+        xs = [inputs.laplace(r, n, device=dev) for r in range(P)]
     comps = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if ef else None
     slows = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if two else None
+    errs = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)] if (ef and unfused) else None
     odt = torch.int16 if out_bf16 else torch.float32
     outs = [torch.empty(n, dtype=odt, device=dev) for _ in range(P)]
     ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits, group), dtype=torch.uint8, device=dev)
@@ -112,7 +137,7 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
     streams = [main] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
     args = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=tiles, group=group,
                               out_dtype=echo.OUT_BF16 if out_bf16 else echo.OUT_F32, ef=ef, comps=comps,
-                              quant=quant, alpha=alpha, beta=beta, slows=slows)
+                              quant=quant, alpha=alpha, beta=beta, slows=slows, errs=errs)
     for _ in range(warmup):
         echo.echo_allreduce_sim(args, streams=streams)
     torch.cuda.synchronize()
@@ -132,25 +157,31 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
     call_ms = {"median": round(per_call[steps // 2], 4), "min": round(per_call[0], 4)}
 
     B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4, group, two)
-    value = P * n * B / (ms_per_step * 1e-3) / 1e9
-    if not time_kernel:
-        del xs, comps, slows, outs, ws
-        torch.cuda.empty_cache()
-        return dict(value=value, ms_per_step=ms_per_step, bytes_per_call=P * n * B, B=B, call_ms=call_ms)
+    if ef and unfused:
+        B += 8                         # e written by the call and read back by the update pass
+    res = dict(value=P * n * B / (ms_per_step * 1e-3) / 1e9, ms_per_step=ms_per_step, bytes_per_call=P * n * B,
+               B=B, call_ms=call_ms, elements_per_s=P * n / (ms_per_step * 1e-3),
+               wall_ms_per_step=wall * 1e3 / steps, event_ms_per_step=ev_ms / steps)
+    if time_kernel:
+        res["roofline"] = push_roofline(echo, torch, xs, comps, ws, P, n, bits, ef)
+    del xs, comps, slows, errs, outs, ws, args
+    torch.cuda.empty_cache()
+    return res
 
-    # dominant kernel: the push of one rank over one tile, timed with events on
-    # the stream it is launched on (the sim launches the same kernel, same size)
+
+def push_roofline(echo, torch, xs, comps, ws, P, n, bits, ef):
+    """The dominant kernel, push quantize of one rank over whole segments
+    (the launch the back-to-back schedule makes), timed with events on the
+    stream it is launched on; codes and params go to the workspace's first
+    rank slots."""
     S = n // P
-    gps = S // G
-    tile_groups = -(-gps // min(tiles, gps))
-    tile_len = tile_groups * G
     reps = max(8, 2 * P)
-    # codes and params of this timing go to the workspace's first rank slots
+    main = torch.cuda.current_stream()
     cb = n // 2 if bits == 4 else n
     codes_t, params_t = ws, ws[((cb + 255) // 256) * 256 * P:]
 
     def push(r):
-        echo.echo_quantize_ef(xs[r], comps[r] if ef else None, n, P, r, 0, tile_len, bits, G,
+        echo.echo_quantize_ef(xs[r], comps[r] if ef else None, n, P, r, 0, S, bits, G,
                               codes_t, params_t, comps[r] if ef else None,
                               echo.ERR_NEGATED if ef else 0, stream=main)
 
@@ -165,27 +196,68 @@ def run_case(echo, torch, inputs, P, n, bits, tiles, nstreams, steps, warmup, ou
     e1.record(main)
     torch.cuda.synchronize()
     push_ms = e0.elapsed_time(e1) / reps
-    push_bytes = (P - 1) * tile_len * push_bytes_per_elem(bits, ef)
+    push_bytes = (P - 1) * S * push_bytes_per_elem(bits, ef)
     achieved = push_bytes / (push_ms * 1e-3) / 1e9
-    traffic = committed_traffic(P, tiles, n)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "echo::push_kernel (echo_quantize_ef)", "launch_elements": (P - 1) * tile_len,
-            "algorithmic_bytes_per_launch": int(push_bytes), "mean_launch_ms": round(push_ms, 4)}
-    del xs, comps, slows, outs, ws
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(P, n),
+            "kernel": "echo::push_kernel (echo_quantize_ef), one rank over whole segments",
+            "launch_elements": (P - 1) * S, "algorithmic_bytes_per_launch": int(push_bytes),
+            "mean_launch_ms": round(push_ms, 4)}
+
+
+def leg(r, extra=None):
+    d = {"value": round(r["value"], 1), "unit": "GB/s", "ms_per_step": round(r["ms_per_step"], 4),
+         "frac_of_peak": round(r["value"] / HBM_PEAK_GBS, 4), "elements_per_s": float(f"{r['elements_per_s']:.4g}"),
+         "call_ms": r["call_ms"], "bytes_per_elem_per_rank": round(r["B"], 5)}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def config_legs(echo, torch, inputs):
+    """Per-call throughput of the single-call, depth-chain, 8-bit-chain and
+    training workloads (one call each, inputs of the workload's recipe),
+    back to back on one stream."""
+    dev = "cuda:0"
+    out = {}
+    P = 4
+    xs = [inputs.single(r).to(dev) for r in range(P)]
+    n = xs[0].numel()
+    r = run_case(echo, torch, inputs, P, n, 4, 1, 1, 200, 20, True, True, time_kernel=False, xs=xs)
+    out["single_call_64x1024"] = leg(r, {"P": P, "n": n, "bits": 4, "ef": "classic", "cache_resident": True,
+                                         "latency_us_median": round(r["call_ms"]["median"] * 1e3, 1)})
+    sigma = inputs.chain_channel_scale(device=dev)
+    for ef in (True, False):
+        xs = [inputs.chain(r, 0, sigma_h=sigma, device=dev) for r in range(P)]
+        n = xs[0].numel()
+        r = run_case(echo, torch, inputs, P, n, 4, 1, 1, 50, 10, True, ef, time_kernel=False, xs=xs)
+        out[f"chain_2048x4096_ef_{'on' if ef else 'off'}"] = leg(r, {"P": P, "n": n, "bits": 4})
+    for ef in (True, False):
+        xs = [inputs.chain8(r, 0, device=dev) for r in range(P)]
+        n = xs[0].numel()
+        r = run_case(echo, torch, inputs, P, n, 8, 1, 1, 50, 10, True, ef, time_kernel=False, xs=xs)
+        out[f"chain8_4096x1024_ef_{'on' if ef else 'off'}"] = leg(r, {"P": P, "n": n, "bits": 8})
+    n = 32 * 4096 * 1024
+    for unfused in (False, True):
+        xs = [inputs.training(r, 0, 0, False, n, device=dev) for r in range(P)]
+        r = run_case(echo, torch, inputs, P, n, 4, 1, 1, 10, 3, True, True, time_kernel=False, xs=xs,
+                     alpha=0.5, beta=0.25, unfused=unfused)
+        name = "training_2^27_two_timescale_" + ("update_pass" if unfused else "fused")
+        out[name] = leg(r, {"P": P, "n": n, "bits": 4, "alpha": 0.5, "beta": 0.25,
+                            "update": "separate echo_compensate pass after the call (e written, then read)"
+                            if unfused else "fused into push and reduce"})
     torch.cuda.empty_cache()
-    return dict(value=value, ms_per_step=ms_per_step, bytes_per_call=P * n * B, B=B, roofline=roof,
-                wall_ms_per_step=wall * 1e3 / steps, event_ms_per_step=ev_ms / steps, call_ms=call_ms)
+    return out
 
 
-def tp_block(echo, torch, inputs, reps=10):
+def tp_block(echo, torch, inputs, reps=10, beside_runs=5):
     """One rank's row-parallel matmul and entry pass at the Llama-3-8B MLP down
     projection with TP = 4 (4096 tokens, hidden 4096, K = 14336/4), random
     weights: the fused echo_gemm_quantize_ef against torch.matmul (hipBLASLt)
     followed by echo_quantize_ef, same compensation and outputs; and the
     two-timescale update (echo_compensate) run beside the next matmul (the
     gate/up projection, N = 2*14336/4) on a second stream, against running
-    the two back to back."""
+    the two back to back, repeated to show the spread of the hidden part."""
     shp = inputs.SHAPES["tpblock"]
     M, N, K, P = shp["tokens"], shp["hidden"], shp["k"], shp["P"]
     n = M * N
@@ -220,6 +292,7 @@ def tp_block(echo, torch, inputs, reps=10):
     t_fused = timed(fused)
     t_gemm = timed(gemm_only)
     t_lib = timed(lib)
+    t_push = timed(push)
     t_lib_push = timed(lambda: (lib(), push()))
     flop = 2.0 * M * N * K
 
@@ -242,23 +315,31 @@ def tp_block(echo, torch, inputs, reps=10):
         ev2.record(side)
         main.wait_event(ev2)
 
-    t_next = timed(nxt)
-    t_upd = timed(lambda: upd(main))
-    t_serial = timed(lambda: (nxt(), upd(main)))
-    t_beside = timed(beside)
+    runs = []
+    for _ in range(beside_runs):
+        t_next = timed(nxt)
+        t_upd = timed(lambda: upd(main))
+        t_serial = timed(lambda: (nxt(), upd(main)))
+        t_beside = timed(beside)
+        hidden = (t_serial - t_beside) / t_upd if t_upd > 0 else 0.0
+        runs.append({"next_matmul_us": round(t_next, 1), "update_us": round(t_upd, 1),
+                     "serial_us": round(t_serial, 1), "beside_us": round(t_beside, 1),
+                     "hidden_fraction": round(hidden, 3)})
+    hid = sorted(r["hidden_fraction"] for r in runs)
     out = {
         "shape": {"M": M, "N": N, "K": K, "P": P, "bits": 4, "ef": "classic, -e in place"},
         "fused_us": round(t_fused, 1),
         "gemm_alone_us": round(t_gemm, 1),
         "hipblaslt_gemm_us": round(t_lib, 1),
+        "push_alone_us": round(t_push, 1),
         "hipblaslt_gemm_plus_push_us": round(t_lib_push, 1),
         "roofline": {"bound": "mfma", "achieved": round(flop / t_fused / 1e6, 1), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(flop / t_fused / 1e6 / 2500.0, 4),
                      "kernel": "echo::gemm256_push_kernel (echo_gemm_quantize_ef)"},
         "gemm_alone_tflops": round(flop / t_gemm / 1e6, 1),
         "hipblaslt_tflops": round(flop / t_lib / 1e6, 1),
-        "update_beside_next_matmul": {"next_matmul_us": round(t_next, 1), "update_us": round(t_upd, 1),
-                                      "serial_us": round(t_serial, 1), "beside_us": round(t_beside, 1)},
+        "update_beside_next_matmul": {"runs": runs, "hidden_fraction_median": hid[len(hid) // 2],
+                                      "hidden_fraction_range": [hid[0], hid[-1]]},
     }
     del a16, w16, comp, codes, params, x_out, y, w2, z, err, slow
     torch.cuda.empty_cache()
@@ -286,52 +367,113 @@ def device_copy_gbs(torch, reps=10):
     return gbs
 
 
-def cpu_baseline(P, n, bits, out_bf16, ef, frac_den=4):
-    """The oracle (single-threaded C) on a bounded sample of the workload:
-    a message 1/frac_den the size (every segment shortened alike), drawn from
-    the same Laplace(0,1) recipe, timed over one whole call; then the same
-    sample in host threads.  Returns (single-threaded, threaded)."""
+# ------------------------------------------------------------- CPU baselines --
+
+def _oracle_call(P, xs, bits, ef, out_bf16):
+    """One whole oracle call over host arrays; returns seconds."""
     import numpy as np
     import oracle
-    from error_feedback_quant_amd import inputs
-    S = n // P
-    L = S // frac_den // G * G            # sampled elements per segment
-    # each rank's sample: P segments of L elements from the same Laplace(0,1)
-    # generator (the CPU generator's stream; the distribution is the workload's)
-    sample = [inputs.as_numpy_u16(inputs.laplace(r, P * L, device="cpu", chunk=1 << 24)) for r in range(P)]
-    m = sample[0].size
-    comps = [np.zeros(m, np.float32) for _ in range(P)] if ef else None
+    comps = [np.zeros(xs[0].size, np.float32) for _ in range(P)] if ef else None
     odt = oracle.OUT_BF16 if out_bf16 else oracle.OUT_F32
     t0 = time.perf_counter()
-    oracle.allreduce(sample, bits=bits, ef=ef, comps=comps, out_dtype=odt)
-    dt = time.perf_counter() - t0
+    oracle.allreduce(xs, bits=bits, ef=ef, comps=comps, out_dtype=odt)
+    return time.perf_counter() - t0
+
+
+def _rate(P, n_per_rank, bits, ef, out_bf16, seconds, cores, sample, extra=None):
     B = bytes_per_elem(P, bits, ef, 2 if out_bf16 else 4)
-    single = {"value": round(P * m * B / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-              "sample": f"one call on {m} of {n} elements per rank (1/{frac_den} of every segment, "
-                        f"same distribution), P={P}, {dt:.2f} s single-threaded",
-              "cpu": host_cpu_model()}
-    # the same call as independent calls on mini messages made of the same
-    # range of every segment (groups and elements are independent), one per
-    # worker thread at a time; the oracle's C entry point releases the GIL
+    d = {"value": round(P * n_per_rank * B / seconds / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+         "sample": sample, "seconds_per_call": round(seconds, 4),
+         "elements_per_s": float(f"{P * n_per_rank / seconds:.4g}")}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def onegb_sample(P, L, base=1 << 22):
+    """Host inputs for a 1 GiB-workload sample of P segments of L elements:
+    Laplace(0,1) draws from the workload's CPU generator (base elements per
+    rank, repeated to length; the oracle's work does not depend on the
+    values)."""
+    import numpy as np
+    from error_feedback_quant_amd import inputs
+    xs = []
+    for r in range(P):
+        b = inputs.as_numpy_u16(inputs.laplace(r, min(base, P * L), device="cpu", chunk=1 << 22))
+        reps = -(-(P * L) // b.size)
+        xs.append(np.ascontiguousarray(np.tile(b, reps)[:P * L]))
+    return xs
+
+
+def cpu_baseline_sampled(P, n, bits, out_bf16, ef, den=64):
+    """The oracle, single-threaded, on 1/den of every segment of the 1 GiB
+    message (tiles are independent, so the work scales exactly), reported
+    for the whole call."""
+    S = n // P
+    L = S // den // G * G
+    xs = onegb_sample(P, L)
+    dt = _oracle_call(P, xs, bits, ef, out_bf16) * (S / L)
+    return _rate(P, n, bits, ef, out_bf16, dt, 1,
+                 f"one call on 1/{den} of every segment ({P}x{L} elements per rank, Laplace(0,1)), "
+                 f"single-threaded, scaled x{S // L} to the 2^29-element call, P={P}",
+                 {"cpu": host_cpu_model()})
+
+
+def cpu_baseline_threaded_full(P, n, bits, out_bf16, ef, workers):
+    """The whole 1 GiB call as independent oracle calls on mini messages made
+    of the same range of every segment (groups and elements are independent),
+    in `workers` host threads (the oracle's C entry point releases the GIL)."""
+    import numpy as np
+    import oracle
     from concurrent.futures import ThreadPoolExecutor
-    workers = host_threads()
-    chunk = max(G, (L // (8 * workers)) // G * G)
-    comps = [np.zeros(m, np.float32) for _ in range(P)] if ef else None
+    S = n // P
+    xs = onegb_sample(P, S)
+    chunk = min(1 << 18, S)
+    assert S % chunk == 0
+    odt = oracle.OUT_BF16 if out_bf16 else oracle.OUT_F32
 
     def one(a0):
-        b0 = min(L, a0 + chunk)
-        xm = [np.concatenate([x[s * L + a0:s * L + b0] for s in range(P)]) for x in sample]
-        cm = [np.concatenate([c[s * L + a0:s * L + b0] for s in range(P)]) for c in comps] if ef else None
+        xm = [np.concatenate([x[s * S + a0:s * S + a0 + chunk] for s in range(P)]) for x in xs]
+        cm = [np.zeros(P * chunk, np.float32) for _ in range(P)] if ef else None
         oracle.allreduce(xm, bits=bits, ef=ef, comps=cm, out_dtype=odt)
 
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=workers) as pool:
-        list(pool.map(one, range(0, L, chunk)))
-    dtt = time.perf_counter() - t0
-    threaded = {"value": round(P * m * B / dtt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
-                "sample": f"the same sample as {-(-L // chunk)} independent calls on ranges of {chunk} elements "
-                          f"of every segment, {workers} threads, {dtt:.2f} s"}
-    return single, threaded
+        list(pool.map(one, range(0, S, chunk)))
+    dt = time.perf_counter() - t0
+    del xs
+    return _rate(P, n, bits, ef, out_bf16, dt, workers,
+                 f"the whole 2^29-element call at P={P} as {S // chunk} independent calls on {chunk}-element "
+                 f"ranges of every segment, {workers} threads")
+
+
+def cpu_baselines(out_bf16=True):
+    """The oracle's timing plan beside the GPU numbers: single-threaded calls
+    of the single-call (whole), depth-chain and 8-bit-chain workloads (one
+    call each), the 1 GiB call at P = 8 (sampled, scaled), and the whole
+    1 GiB call in host threads at P = 4 and 8."""
+    from error_feedback_quant_amd import inputs
+    P = 4
+    res = {"nproc": os.cpu_count(), "threads_available": host_threads(1 << 30), "cpu": host_cpu_model()}
+    xs = [inputs.as_numpy_u16(inputs.single(r)) for r in range(P)]
+    dt = _oracle_call(P, xs, 4, True, out_bf16)
+    res["single_call_64x1024"] = _rate(P, xs[0].size, 4, True, out_bf16, dt, 1, "one whole call, single-threaded")
+    sigma = inputs.chain_channel_scale()
+    for ef in (True, False):
+        xs = [inputs.as_numpy_u16(inputs.chain(r, 0, sigma_h=sigma)) for r in range(P)]
+        dt = _oracle_call(P, xs, 4, ef, out_bf16)
+        res[f"chain_2048x4096_ef_{'on' if ef else 'off'}"] = _rate(P, xs[0].size, 4, ef, out_bf16, dt, 1,
+                                                                   "one whole call, single-threaded")
+    for ef in (True, False):
+        xs = [inputs.as_numpy_u16(inputs.chain8(r, 0)) for r in range(P)]
+        dt = _oracle_call(P, xs, 8, ef, out_bf16)
+        res[f"chain8_4096x1024_ef_{'on' if ef else 'off'}"] = _rate(P, xs[0].size, 8, ef, out_bf16, dt, 1,
+                                                                    "one whole call, single-threaded")
+    res["onegb_p8_sampled"] = cpu_baseline_sampled(8, N_1GIB, 4, out_bf16, True)
+    workers = host_threads()
+    for Pt in (4, 8):
+        res[f"onegb_p{Pt}_threaded_whole_call"] = cpu_baseline_threaded_full(Pt, N_1GIB, 4, out_bf16, True, workers)
+    return res
 
 
 def host_threads(cap: int = 16) -> int:
@@ -362,20 +504,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--P", type=int, default=4)
     ap.add_argument("--bits", type=int, default=4, choices=[4, 8])
-    ap.add_argument("--tiles", type=int, default=1)
-    ap.add_argument("--streams", type=int, default=1)
-    ap.add_argument("--staged-tiles", type=int, default=4)
-    ap.add_argument("--staged-streams", type=int, default=4)
-    ap.add_argument("--no-staged", action="store_true", help="skip the staged-schedule leg")
+    ap.add_argument("--tiles", type=int, default=STAGED_TILES)
+    ap.add_argument("--streams", type=int, default=STAGED_STREAMS)
+    ap.add_argument("--no-serial", action="store_true", help="skip the back-to-back schedule leg")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the Table 8 quantizer/group-size legs")
     ap.add_argument("--out", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--no-ef", action="store_true")
     ap.add_argument("--no-modes", action="store_true",
-                    help="skip the feedback-off, fp32-output and two-timescale legs")
+                    help="skip the feedback-off, fp32-output, two-timescale and 8-bit legs")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload call legs")
     ap.add_argument("--no-p8", action="store_true", help="skip the P=8 leg")
     ap.add_argument("--no-tp", action="store_true", help="skip the fused matmul + entry pass leg")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     a = ap.parse_args()
@@ -395,13 +536,13 @@ def main():
     out_bf16 = a.out == "bf16"
     ef = not a.no_ef
     main_res = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, a.steps, a.warmup,
-                        out_bf16, ef)
-    staged = None
-    if not a.no_staged:
-        rs = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.staged_tiles, a.staged_streams,
-                      max(5, a.steps // 2), a.warmup, out_bf16, ef, time_kernel=False)
-        staged = {"tiles": a.staged_tiles, "streams": a.staged_streams, "value": round(rs["value"], 1),
-                  "ms_per_step": round(rs["ms_per_step"], 4), "frac_of_peak": round(rs["value"] / HBM_PEAK_GBS, 4)}
+                        out_bf16, ef, time_kernel=False)
+    serial = None
+    roof = None
+    if not a.no_serial:
+        rs = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, 1, 1, a.steps, a.warmup, out_bf16, ef)
+        roof = rs.pop("roofline")
+        serial = leg(rs, {"tiles": 1, "streams": 1, "schedule": schedule_name(1, 1)})
     variants = None
     if not a.no_variants:
         variants = {}
@@ -409,8 +550,7 @@ def main():
                                    ("zero_aware_g256", "zero_aware", 256)):
             rv = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 3),
                           a.warmup, out_bf16, ef, time_kernel=False, quant=quant, group=group)
-            variants[name] = {"value": round(rv["value"], 1), "ms_per_step": round(rv["ms_per_step"], 4),
-                              "frac_of_peak": round(rv["value"] / HBM_PEAK_GBS, 4)}
+            variants[name] = leg(rv)
     modes = None
     if not a.no_modes:
         # the same call with feedback off, with fp32 output, with the
@@ -425,17 +565,19 @@ def main():
                 (f"bits{other_bits}", ef, out_bf16, 1.0, 0.0, other_bits)):
             rm = run_case(echo, torch, inputs, a.P, N_1GIB, m_bits, a.tiles, a.streams, max(5, a.steps // 3),
                           a.warmup, m_bf16, m_ef, time_kernel=False, alpha=alpha, beta=beta)
-            modes[name] = {"value": round(rm["value"], 1), "ms_per_step": round(rm["ms_per_step"], 4),
-                           "bytes_per_elem_per_rank": round(rm["B"], 5),
-                           "frac_of_peak": round(rm["value"] / HBM_PEAK_GBS, 4)}
-    copy_gbs = device_copy_gbs(torch)
-    tp = None if a.no_tp else tp_block(echo, torch, inputs)
+            modes[name] = leg(rm)
     p8 = None
     if not a.no_p8 and a.P != 8:
         r8 = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 2),
-                      a.warmup, out_bf16, ef)
-        p8 = {"value": round(r8["value"], 1), "ms_per_step": round(r8["ms_per_step"], 4),
-              "frac_of_peak": round(r8["value"] / HBM_PEAK_GBS, 4), "roofline": r8["roofline"]}
+                      a.warmup, out_bf16, ef, time_kernel=False)
+        r8s = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, 1, 1, max(5, a.steps // 2), a.warmup, out_bf16, ef)
+        roof8 = r8s.pop("roofline")
+        p8 = leg(r8, {"tiles": a.tiles, "streams": a.streams, "schedule": schedule_name(a.tiles, a.streams),
+                      "roofline": roof8,
+                      "serial": leg(r8s, {"tiles": 1, "streams": 1, "schedule": schedule_name(1, 1)})})
+    configs = None if a.no_configs else config_legs(echo, torch, inputs)
+    copy_gbs = device_copy_gbs(torch)
+    tp = None if a.no_tp else tp_block(echo, torch, inputs)
     if a.calib_copy:
         src = torch.empty(N_1GIB, dtype=torch.int16, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
@@ -443,9 +585,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cpu = cpu_threaded = None
+    cpu = cpu_plan = None
     if not a.no_cpu:
-        cpu, cpu_threaded = cpu_baseline(a.P, N_1GIB, a.bits, out_bf16, ef)
+        cpu = cpu_baseline_sampled(a.P, N_1GIB, a.bits, out_bf16, ef)
+        cpu_plan = cpu_baselines(out_bf16)
 
     line = {
         "metric": METRIC,
@@ -463,24 +606,24 @@ def main():
         "config": {
             "workload": f"1 GiB message: 2^29 bf16 elements per rank, Laplace(0,1), P={a.P} simulated ranks",
             "P": a.P, "bits": a.bits, "group": G, "tiles": a.tiles, "streams": a.streams,
-            "schedule": ("push, reduce and tail back to back on one stream, the fastest on one GPU; "
-                         "the tile-staged multi-stream schedule is reported under 'staged'")
-                        if (a.tiles, a.streams) == (1, 1) else "tile-staged across streams",
+            "schedule": schedule_name(a.tiles, a.streams),
             "ef": "classic error feedback (alpha=1), -e written in place" if ef else "off",
             "out": a.out, "bytes_per_elem_per_rank": round(main_res["B"], 5),
             "bytes_per_call": int(main_res["bytes_per_call"]),
             "frac_of_peak": round(main_res["value"] / HBM_PEAK_GBS, 4),
+            "elements_per_s": float(f"{main_res['elements_per_s']:.4g}"),
             "call_ms": main_res["call_ms"],
             "device_copy_gbs": round(copy_gbs, 1),
             "frac_of_device_copy": round(main_res["value"] / copy_gbs, 4),
         },
-        "roofline": main_res["roofline"],
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "cpu_baseline_threaded": cpu_threaded,
-        "staged": staged,
+        "serial": serial,
+        "p8": p8,
+        "configs": configs,
+        "cpu_baselines": cpu_plan,
         "variants": variants,
         "modes": modes,
-        "p8": p8,
         "tp_block": tp,
     }
     print(json.dumps(line), flush=True)

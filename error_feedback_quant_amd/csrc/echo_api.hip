@@ -523,38 +523,48 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
     const int flags = ((fused && !two_fused) ? ECHO_ERR_NEGATED : 0) | a->quant;
     echo::UpdArgs upd_r[ECHO_MAX_P];
     for (int r = 0; r < P; ++r) upd_r[r] = make_upd(a->slow[r], a->alpha, a->beta);
-    for (int64_t t = 0; t < T; ++t) {
-        const int64_t tb = t * tile_len;
-        const int64_t tl = (tb + tile_len <= S) ? tile_len : S - tb;
-        // push: every rank quantizes its non-owned segments of this tile
-        for (int r = 0; r < P; ++r) {
-            const float* c = a->ef ? a->comp[r] : nullptr;
-            float* e = a->ef ? (fused ? a->comp[r] : a->err[r]) : nullptr;
-            rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, a->group, (uint8_t*)pc[r],
-                             (echo_qparam*)pp[r], two_fused ? nullptr : e, flags,
-                             two_fused ? &upd_r[r] : nullptr, s_push);
-            if (rc) return rc;
+    // The tail of tile t is enqueued after the push of tile t + 1, so that the
+    // reduce of a tile can run beside the next tile's push even when the tail
+    // shares the push's stream (two streams).
+    auto tile_at = [&](int64_t t, int64_t& tb, int64_t& tl) {
+        tb = t * tile_len;
+        tl = (tb + tile_len <= S) ? tile_len : S - tb;
+    };
+    for (int64_t t = 0; t <= T; ++t) {
+        int64_t tb, tl;
+        if (t < T) {
+            tile_at(t, tb, tl);
+            // push: every rank quantizes its non-owned segments of this tile
+            for (int r = 0; r < P; ++r) {
+                const float* c = a->ef ? a->comp[r] : nullptr;
+                float* e = a->ef ? (fused ? a->comp[r] : a->err[r]) : nullptr;
+                rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, a->group, (uint8_t*)pc[r],
+                                 (echo_qparam*)pp[r], two_fused ? nullptr : e, flags,
+                                 two_fused ? &upd_r[r] : nullptr, s_push);
+                if (rc) return rc;
+            }
+            if (multi) {
+                if ((he = hipEventRecord(ev_push(t), s_push)) != hipSuccess) return hip_fail(he);
+                if ((he = hipStreamWaitEvent(s_red, ev_push(t), 0)) != hipSuccess) return hip_fail(he);
+            }
+            // reduce: every owner sums its segment of this tile and requantizes once
+            for (int o = 0; o < P; ++o) {
+                const float* c = a->ef ? a->comp[o] : nullptr;
+                float* e = a->ef ? (fused ? a->comp[o] : a->err[o]) : nullptr;
+                rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, a->group, sc, sp,
+                                   two_fused ? nullptr : e, flags, two_fused ? &upd_r[o] : nullptr, s_red);
+                if (rc) return rc;
+            }
+            if (multi && (he = hipEventRecord(ev_red(t), s_red)) != hipSuccess) return hip_fail(he);
         }
-        if (multi) {
-            if ((he = hipEventRecord(ev_push(t), s_push)) != hipSuccess) return hip_fail(he);
-            if ((he = hipStreamWaitEvent(s_red, ev_push(t), 0)) != hipSuccess) return hip_fail(he);
-        }
-        // reduce: every owner sums its segment of this tile and requantizes once
-        for (int o = 0; o < P; ++o) {
-            const float* c = a->ef ? a->comp[o] : nullptr;
-            float* e = a->ef ? (fused ? a->comp[o] : a->err[o]) : nullptr;
-            rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, a->group, sc, sp,
-                               two_fused ? nullptr : e, flags, two_fused ? &upd_r[o] : nullptr, s_red);
-            if (rc) return rc;
-        }
-        if (multi) {
-            if ((he = hipEventRecord(ev_red(t), s_red)) != hipSuccess) return hip_fail(he);
-            if ((he = hipStreamWaitEvent(s_tail, ev_red(t), 0)) != hipSuccess) return hip_fail(he);
-        }
-        // gather moves no bytes here; tail: every rank decodes this tile of every segment
-        for (int r = 0; r < P; ++r) {
-            rc = launch_gather(sc, sp, n, tb, tl, P, a->bits, a->group, a->out[r], a->out_dtype, s_tail);
-            if (rc) return rc;
+        if (t >= 1) {
+            // gather moves no bytes here; tail: every rank decodes tile t - 1 of every segment
+            tile_at(t - 1, tb, tl);
+            if (multi && (he = hipStreamWaitEvent(s_tail, ev_red(t - 1), 0)) != hipSuccess) return hip_fail(he);
+            for (int r = 0; r < P; ++r) {
+                rc = launch_gather(sc, sp, n, tb, tl, P, a->bits, a->group, a->out[r], a->out_dtype, s_tail);
+                if (rc) return rc;
+            }
         }
     }
     // compensator update (two-timescale or unfused) after the last reduce

@@ -248,7 +248,9 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
  *
  * Stage k of every tile runs on streams[k % nstreams] (push 0, reduce 1,
  * tail 2, compensator 3); events order tile t's reduce after its pushes and
- * its tail after its reduce.  The gather moves no bytes here: the tail reads
+ * its tail after its reduce.  Tile t's tail is enqueued after tile t+1's
+ * push, so with two streams (the tail sharing the push's stream) the reduce
+ * of a tile still runs beside the push of the next.  The gather moves no bytes here: the tail reads
  * the owners' sum codes directly.  All streams start after the work already
  * enqueued on streams[0], and streams[0] waits for all of them before the
  * call returns, so the caller may treat the call as enqueued on streams[0].

@@ -48,12 +48,21 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_cpu_baselines_report_the_contract_fields():
-    """Both oracle baselines (single-threaded, and the same sample in host
-    threads) carry value, unit, cores, kind and a sample description, on a
-    small message here."""
-    single, threaded = bench.cpu_baseline(4, 4 * 128 * 256, 4, True, True)
+    """The oracle baselines (single-threaded on a sample of every segment,
+    and whole calls in host threads) carry value, unit, cores, kind and a
+    sample description, on a small message here."""
+    n = 4 * 64 * 256
+    single = bench.cpu_baseline_sampled(4, n, 4, True, True)
+    threaded = bench.cpu_baseline_threaded_full(4, n, 4, True, True, 2)
     for d in (single, threaded):
-        assert set(("value", "unit", "cores", "kind", "sample")) <= set(d)
+        assert set(("value", "unit", "cores", "kind", "sample", "elements_per_s")) <= set(d)
         assert d["unit"] == "GB/s" and d["kind"] == "oracle" and d["value"] > 0
     assert single["cores"] == 1 and "cpu" in single
-    assert 1 <= threaded["cores"] <= 16
+    assert threaded["cores"] == 2
+
+
+def test_two_timescale_state_bytes():
+    """The fused two-timescale update reads c and M and writes c' and M':
+    16 bytes of state per element instead of classic feedback's 8."""
+    fused = bench.bytes_per_elem(4, 4, True, 2, 128, True)
+    assert fused == pytest.approx(2 + 2 + 16 + 0.53125 * (3 - 0.25))
