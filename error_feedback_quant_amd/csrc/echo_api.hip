@@ -34,6 +34,8 @@ constexpr size_t kReduceCompLds = 32 * 1024;
 // tiles per segment in one simulated call: results do not depend on the
 // tiling, and each tile takes two events from the pool
 constexpr int64_t kMaxTiles = 4096;
+// below this many push blocks per rank launch, one launch serves all ranks
+constexpr int64_t kBatchBelowBlocks = 4096;
 
 int hip_fail(hipError_t e)
 {
@@ -127,21 +129,24 @@ struct ReduceL {
         // residency to five blocks per CU (160 KB of LDS): with the
         // compensation stream that measured faster than the six that the
         // registers allow, while the reduce without it wants every wave it
-        // can get and takes no LDS at all.
+        // can get and takes no LDS at all.  Every slot of a launch has the
+        // same streams, so slot 0 decides.
         using Io = echo::Fp32Io<kURed, UP>;
-        size_t lds = (UP || a.comp || a.err) ? Io::kLdsFloats * sizeof(float) : 0;
-        if ((UP || a.comp) && lds < kReduceCompLds) lds = kReduceCompLds;
+        const bool comp = a.comp[0] != nullptr, err = a.err[0] != nullptr;
+        size_t lds = (UP || comp || err) ? Io::kLdsFloats * sizeof(float) : 0;
+        if ((UP || comp) && lds < kReduceCompLds) lds = kReduceCompLds;
         hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G>), grid, dim3(echo::kBlock), lds, st, a);
     }
 };
 
 // ---------------------------------------------------------------- launchers --
-// Each assumes validated arguments and tile_len > 0.
+// Each assumes validated arguments and tile_len > 0.  One launch covers
+// `slots` ranks (or owners): slot k of the pointer arrays belongs to rank
+// (owner) rank0 + k.
 
-echo::UpdArgs make_upd(float* slow, float alpha, float beta)
+echo::UpdArgs make_upd(float alpha, float beta)
 {
     echo::UpdArgs u;
-    u.slow = slow;
     u.alpha = alpha;
     u.beta = beta;
     u.one_minus_alpha = 1.0f - alpha;
@@ -149,41 +154,39 @@ echo::UpdArgs make_upd(float* slow, float alpha, float beta)
     return u;
 }
 
-// upd != nullptr: fused two-timescale update (comp and upd->slow in place, err unused)
-int launch_push(const uint16_t* x, const float* comp, int64_t n, int P, int rank, int64_t tb,
-                int64_t tl, int bits, int group, uint8_t* codes, echo_qparam* params, float* err,
-                int flags, const echo::UpdArgs* upd, hipStream_t st)
+// The scalar fields of a push launch over the tile [tb, tb + tl) of every segment.
+echo::PushArgs push_args(int64_t n, int P, int64_t tb, int64_t tl, int rank0, int flags)
 {
-    if (P == 1) return ECHO_OK;   // a single rank owns everything: nothing to push
     echo::PushArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.x = x; a.comp = comp; a.codes = codes; a.params = (uint32_t*)params; a.err = err;
     a.S = n / P; a.tile_begin = tb; a.tile_rows = (uint32_t)(tl / echo::kRow);
-    a.rank = rank; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
-    if (upd) a.upd = *upd;
-    dim3 grid(blocks_for(a.tile_rows, kUPush), (unsigned)(P - 1));
-    dispatch<PushL>(bits, upd != nullptr, quant_of(flags), group, a, grid, st);
+    a.rank0 = rank0; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    return a;
+}
+
+// upd: the fused two-timescale update (comp and slow in place, err unused)
+int launch_push(const echo::PushArgs& a, int P, int slots, int bits, int group, int flags, bool upd,
+                hipStream_t st)
+{
+    if (P == 1) return ECHO_OK;   // a single rank owns everything: nothing to push
+    dim3 grid(blocks_for(a.tile_rows, kUPush), (unsigned)(P - 1), (unsigned)slots);
+    dispatch<PushL>(bits, upd, quant_of(flags), group, a, grid, st);
     return check_launch();
 }
 
-int launch_reduce(const uint16_t* x, const float* comp, const uint8_t* const* pc,
-                  const echo_qparam* const* pp, int P, int owner, int64_t n, int64_t tb, int64_t tl,
-                  int bits, int group, uint8_t* sc, echo_qparam* sp, float* err, int flags,
-                  const echo::UpdArgs* upd, hipStream_t st)
+echo::ReduceArgs reduce_args(int64_t n, int P, int64_t tb, int64_t tl, int owner0, int flags)
 {
     echo::ReduceArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.x = x; a.comp = comp;
-    for (int j = 0; j < P; ++j) {
-        a.pc[j] = j == owner ? nullptr : pc[j];
-        a.pp[j] = j == owner ? nullptr : (const uint32_t*)pp[j];
-    }
-    a.sc = sc; a.sp = (uint32_t*)sp; a.err = err;
     a.S = n / P; a.tile_begin = tb; a.tile_rows = (uint32_t)(tl / echo::kRow);
-    a.P = P; a.owner = owner; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
-    if (upd) a.upd = *upd;
-    dim3 grid(blocks_for(a.tile_rows, kURed), 1);
-    dispatch<ReduceL>(bits, upd != nullptr, quant_of(flags), group, a, grid, st);
+    a.P = P; a.owner0 = owner0; a.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+    return a;
+}
+
+int launch_reduce(const echo::ReduceArgs& a, int slots, int bits, int group, int flags, bool upd, hipStream_t st)
+{
+    dim3 grid(blocks_for(a.tile_rows, kURed), (unsigned)slots);
+    dispatch<ReduceL>(bits, upd, quant_of(flags), group, a, grid, st);
     return check_launch();
 }
 
@@ -193,13 +196,18 @@ void gather_go(const echo::GatherArgs& a, dim3 grid, hipStream_t st)
     hipLaunchKernelGGL((echo::gather_kernel<B, BF, kUGath, G>), grid, dim3(echo::kBlock), 0, st, a);
 }
 
-int launch_gather(const uint8_t* sc, const echo_qparam* sp, int64_t n, int64_t tb, int64_t tl, int P,
-                  int bits, int group, void* out, int out_dtype, hipStream_t st)
+echo::GatherArgs gather_args(const uint8_t* sc, const echo_qparam* sp, int64_t n, int P, int64_t tb, int64_t tl)
 {
     echo::GatherArgs a;
-    a.sc = sc; a.sp = (const uint32_t*)sp; a.out = out;
+    std::memset(&a, 0, sizeof(a));
+    a.sc = sc; a.sp = (const uint32_t*)sp;
     a.S = n / P; a.tile_begin = tb; a.tile_rows = (uint32_t)(tl / echo::kRow);
-    dim3 grid(blocks_for(a.tile_rows, kUGath), (unsigned)P);
+    return a;
+}
+
+int launch_gather(const echo::GatherArgs& a, int P, int slots, int bits, int group, int out_dtype, hipStream_t st)
+{
+    dim3 grid(blocks_for(a.tile_rows, kUGath), (unsigned)P, (unsigned)slots);
     const bool bf = out_dtype == ECHO_OUT_BF16;
     if (bits == 4) {
         if (group == 128) { if (bf) gather_go<4, true, 128>(a, grid, st); else gather_go<4, false, 128>(a, grid, st); }
@@ -216,8 +224,8 @@ int launch_compensate(const float* err, float* comp, float* slow, int64_t n, flo
 {
     if (n == 0) return ECHO_OK;
     echo::CompArgs a;
-    a.err = err; a.comp = comp; a.n = n;
-    a.upd = make_upd(slow, alpha, beta);
+    a.err = err; a.comp = comp; a.slow = slow; a.n = n;
+    a.upd = make_upd(alpha, beta);
     int64_t chunks = (n + 3) / 4;
     int64_t blocks = (chunks + echo::kBlock - 1) / echo::kBlock;
     if (blocks > 8192) blocks = 8192;
@@ -311,8 +319,9 @@ int echo_quantize_ef(const uint16_t* x_bf16, const float* comp, int64_t n, int P
     if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(params) ||
         (comp && !aligned16(comp)) || (err && !aligned16(err)))
         return ECHO_EALIGN;
-    return launch_push(x_bf16, comp, n, P, rank, tile_begin, tile_len, bits, group, codes, params, err,
-                       flags, nullptr, (hipStream_t)stream);
+    echo::PushArgs a = push_args(n, P, tile_begin, tile_len, rank, flags);
+    a.x[0] = x_bf16; a.comp[0] = comp; a.codes[0] = codes; a.params[0] = (uint32_t*)params; a.err[0] = err;
+    return launch_push(a, P, 1, bits, group, flags, false, (hipStream_t)stream);
 }
 
 int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_t M, int64_t N,
@@ -386,8 +395,14 @@ int echo_reduce_segment(const uint16_t* own_x_bf16, const float* own_comp,
     if (!aligned16(own_x_bf16) || !aligned16(sum_codes) || !aligned16(sum_params) ||
         (own_comp && !aligned16(own_comp)) || (own_err && !aligned16(own_err)))
         return ECHO_EALIGN;
-    return launch_reduce(own_x_bf16, own_comp, peer_codes, peer_params, P, owner, n, tile_begin, tile_len,
-                         bits, group, sum_codes, sum_params, own_err, flags, nullptr, (hipStream_t)stream);
+    echo::ReduceArgs a = reduce_args(n, P, tile_begin, tile_len, owner, flags);
+    a.x[0] = own_x_bf16; a.comp[0] = own_comp; a.err[0] = own_err;
+    for (int j = 0; j < P; ++j) {
+        a.pc[j] = j == owner ? nullptr : peer_codes[j];
+        a.pp[j] = j == owner ? nullptr : (const uint32_t*)peer_params[j];
+    }
+    a.sc = sum_codes; a.sp = (uint32_t*)sum_params;
+    return launch_reduce(a, 1, bits, group, flags, false, (hipStream_t)stream);
 }
 
 int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params, int64_t n,
@@ -400,8 +415,9 @@ int echo_gather_dequant(const uint8_t* sum_codes, const echo_qparam* sum_params,
     if (n == 0 || tile_len == 0) return ECHO_OK;
     if (!sum_codes || !sum_params || !out) return ECHO_EINVAL;
     if (!aligned16(sum_codes) || !aligned16(sum_params) || !aligned16(out)) return ECHO_EALIGN;
-    return launch_gather(sum_codes, sum_params, n, tile_begin, tile_len, P, bits, group, out, out_dtype,
-                         (hipStream_t)stream);
+    echo::GatherArgs a = gather_args(sum_codes, sum_params, n, P, tile_begin, tile_len);
+    a.out[0] = out;
+    return launch_gather(a, P, 1, bits, group, out_dtype, (hipStream_t)stream);
 }
 
 int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n, float alpha, float beta,
@@ -521,8 +537,19 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
     // then echo_compensate after the last reduce)
     const bool two_fused = a->ef && fused && a->beta > 0.0f;
     const int flags = ((fused && !two_fused) ? ECHO_ERR_NEGATED : 0) | a->quant;
-    echo::UpdArgs upd_r[ECHO_MAX_P];
-    for (int r = 0; r < P; ++r) upd_r[r] = make_upd(a->slow[r], a->alpha, a->beta);
+    const echo::UpdArgs upd = make_upd(a->alpha, a->beta);
+    // Small tiles: one launch per stage serves every rank (the per-rank
+    // launches would be too small to fill the GPU, and the call is bound by
+    // launch latency).  Large tiles: one launch per rank, which measured
+    // faster than one launch over all ranks.
+    const bool batch = (int64_t)blocks_for((uint32_t)(tile_len / echo::kRow), kUPush) * (P - 1) < kBatchBelowBlocks;
+    const int per_launch = batch ? P : 1;
+    auto comp_of = [&](int r) -> float* { return a->ef ? a->comp[r] : nullptr; };
+    auto err_of = [&](int r) -> float* {
+        return (a->ef && !two_fused) ? (fused ? a->comp[r] : a->err[r]) : nullptr;
+    };
+    auto slow_of = [&](int r) -> float* { return two_fused ? a->slow[r] : nullptr; };
+
     // The tail of tile t is enqueued after the push of tile t + 1, so that the
     // reduce of a tile can run beside the next tile's push even when the tail
     // shares the push's stream (two streams).
@@ -535,25 +562,31 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
         if (t < T) {
             tile_at(t, tb, tl);
             // push: every rank quantizes its non-owned segments of this tile
-            for (int r = 0; r < P; ++r) {
-                const float* c = a->ef ? a->comp[r] : nullptr;
-                float* e = a->ef ? (fused ? a->comp[r] : a->err[r]) : nullptr;
-                rc = launch_push(a->x[r], c, n, P, r, tb, tl, a->bits, a->group, (uint8_t*)pc[r],
-                                 (echo_qparam*)pp[r], two_fused ? nullptr : e, flags,
-                                 two_fused ? &upd_r[r] : nullptr, s_push);
-                if (rc) return rc;
+            for (int r0 = 0; r0 < P; r0 += per_launch) {
+                echo::PushArgs pa = push_args(n, P, tb, tl, r0, flags);
+                pa.upd = upd;
+                for (int k = 0; k < per_launch; ++k) {
+                    const int r = r0 + k;
+                    pa.x[k] = a->x[r]; pa.comp[k] = comp_of(r); pa.err[k] = err_of(r); pa.slow[k] = slow_of(r);
+                    pa.codes[k] = (uint8_t*)pc[r]; pa.params[k] = (uint32_t*)pp[r];
+                }
+                if ((rc = launch_push(pa, P, per_launch, a->bits, a->group, flags, two_fused, s_push))) return rc;
             }
             if (multi) {
                 if ((he = hipEventRecord(ev_push(t), s_push)) != hipSuccess) return hip_fail(he);
                 if ((he = hipStreamWaitEvent(s_red, ev_push(t), 0)) != hipSuccess) return hip_fail(he);
             }
             // reduce: every owner sums its segment of this tile and requantizes once
-            for (int o = 0; o < P; ++o) {
-                const float* c = a->ef ? a->comp[o] : nullptr;
-                float* e = a->ef ? (fused ? a->comp[o] : a->err[o]) : nullptr;
-                rc = launch_reduce(a->x[o], c, pc, pp, P, o, n, tb, tl, a->bits, a->group, sc, sp,
-                                   two_fused ? nullptr : e, flags, two_fused ? &upd_r[o] : nullptr, s_red);
-                if (rc) return rc;
+            for (int o0 = 0; o0 < P; o0 += per_launch) {
+                echo::ReduceArgs ra = reduce_args(n, P, tb, tl, o0, flags);
+                ra.upd = upd;
+                for (int k = 0; k < per_launch; ++k) {
+                    const int o = o0 + k;
+                    ra.x[k] = a->x[o]; ra.comp[k] = comp_of(o); ra.err[k] = err_of(o); ra.slow[k] = slow_of(o);
+                }
+                for (int j = 0; j < P; ++j) { ra.pc[j] = pc[j]; ra.pp[j] = (const uint32_t*)pp[j]; }
+                ra.sc = sc; ra.sp = (uint32_t*)sp;
+                if ((rc = launch_reduce(ra, per_launch, a->bits, a->group, flags, two_fused, s_red))) return rc;
             }
             if (multi && (he = hipEventRecord(ev_red(t), s_red)) != hipSuccess) return hip_fail(he);
         }
@@ -561,9 +594,10 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
             // gather moves no bytes here; tail: every rank decodes tile t - 1 of every segment
             tile_at(t - 1, tb, tl);
             if (multi && (he = hipStreamWaitEvent(s_tail, ev_red(t - 1), 0)) != hipSuccess) return hip_fail(he);
-            for (int r = 0; r < P; ++r) {
-                rc = launch_gather(sc, sp, n, tb, tl, P, a->bits, a->group, a->out[r], a->out_dtype, s_tail);
-                if (rc) return rc;
+            for (int r0 = 0; r0 < P; r0 += per_launch) {
+                echo::GatherArgs ga = gather_args(sc, sp, n, P, tb, tl);
+                for (int k = 0; k < per_launch; ++k) ga.out[k] = a->out[r0 + k];
+                if ((rc = launch_gather(ga, P, per_launch, a->bits, a->group, a->out_dtype, s_tail))) return rc;
             }
         }
     }

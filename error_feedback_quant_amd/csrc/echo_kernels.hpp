@@ -519,7 +519,6 @@ struct Fp32Io {
 // the compensation and slow-memory buffers -- the same IEEE operations, in the
 // same order, as compensate_kernel, so the results are bit-identical.
 struct UpdArgs {
-    float* slow;
     float alpha, beta, one_minus_alpha, one_minus_beta;
 };
 
@@ -533,22 +532,25 @@ __device__ __forceinline__ void update1(const UpdArgs& a, float e, float m, floa
     m_out = m1 + m2;
 }
 
+// One launch serves one rank or several: blockIdx.z picks slot z of the
+// per-rank arrays, for rank rank0 + z.
 struct PushArgs {
-    const uint16_t* x;
-    const float* comp;      // nullable
-    uint8_t* codes;
-    uint32_t* params;
-    float* err;             // nullable, may alias comp
-    int64_t S;              // segment length
-    int64_t tile_begin;     // tile start inside each segment
-    uint32_t tile_rows;     // 128-element rows per segment tile (>= 1)
-    int rank;
+    const uint16_t* x[kMaxP];
+    const float* comp[kMaxP];   // nullable (the same for every slot)
+    uint8_t* codes[kMaxP];
+    uint32_t* params[kMaxP];
+    float* err[kMaxP];          // nullable, may alias comp
+    float* slow[kMaxP];         // UPD kernels only
+    int64_t S;                  // segment length
+    int64_t tile_begin;         // tile start inside each segment
+    uint32_t tile_rows;         // 128-element rows per segment tile (>= 1)
+    int rank0;
     int negate;
-    UpdArgs upd;            // UPD kernels only: comp is updated in place
+    UpdArgs upd;                // UPD kernels only: comp and slow are updated in place
 };
 
-// grid: (ceil(tile_rows / (16 U)), P - 1); blockIdx.y = index among the
-// segments this rank does not own.  UPD: comp and upd.slow are required and
+// grid: (ceil(tile_rows / (16 U)), P - 1, ranks); blockIdx.y = index among the
+// segments the rank does not own.  UPD: comp and slow are required and
 // updated in place (err unused).
 template <int BITS, int U, bool UPD, int QUANT, int GROUP>
 __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
@@ -559,12 +561,20 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = lane & 15u;
     const uint32_t rw = lane >> 4;                       // this lane's row in the wave
+    const uint32_t z = blockIdx.z;
+    const uint32_t rank = (uint32_t)a.rank0 + z;
     const uint32_t si = blockIdx.y;
-    const uint32_t seg = si + (si >= (uint32_t)a.rank ? 1u : 0u);
+    const uint32_t seg = si + (si >= rank ? 1u : 0u);
     const int64_t seg0 = (int64_t)seg * a.S + a.tile_begin;
     const uint32_t last = a.tile_rows - 1u;
-    const bool has_comp = UPD || a.comp != nullptr;
-    const bool has_out = UPD || a.err != nullptr;
+    const uint16_t* const x = a.x[z];
+    float* const comp = (float*)a.comp[z];
+    float* const slow = a.slow[z];
+    float* const err = a.err[z];
+    uint8_t* const codes = a.codes[z];
+    uint32_t* const params = a.params[z];
+    const bool has_comp = UPD || comp != nullptr;
+    const bool has_out = UPD || err != nullptr;
 
     WaveMap wm[U];
     u32x4 xv[U];
@@ -576,8 +586,8 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
         wm[k].last = last;
         wm[k].lane = lane;
         const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
-        xv[k] = ld_stream((const u32x4*)(a.x + e0));
-        if (has_comp) io.load(k, wm[k], a.comp, a.upd.slow);
+        xv[k] = ld_stream((const u32x4*)(x + e0));
+        if (has_comp) io.load(k, wm[k], comp, slow);
     }
     if (has_comp) io.stage(lds, wave, lane);
 #pragma unroll
@@ -594,7 +604,7 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
             for (int i = 0; i < 8; ++i) u[i] += c[i];
         }
         float q[8], e[8];
-        const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.codes, a.params, q);
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, codes, params, q);
         if (UPD) {
             group_error(q, p, u, false, e);
             float m[8], cn[8], mn[8];
@@ -608,30 +618,33 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
             io.put(lds, k, 0, wave, lane, e);
         }
     }
-    if (has_out) io.flush(lds, wave, lane, wm, UPD ? (float*)a.comp : a.err, a.upd.slow);
+    if (has_out) io.flush(lds, wave, lane, wm, UPD ? comp : err, slow);
 }
 
 // ------------------------------------------------------------ owner reduce --
 
+// One launch serves one owner or several: blockIdx.y picks slot y of the
+// per-owner arrays, for owner owner0 + y.
 struct ReduceArgs {
-    const uint16_t* x;              // owner's partial sums
-    const float* comp;              // owner's compensation, nullable
-    const uint8_t* pc[kMaxP];       // push codes of each rank ([owner] unused)
+    const uint16_t* x[kMaxP];       // owner's partial sums
+    const float* comp[kMaxP];       // owner's compensation, nullable
+    float* err[kMaxP];              // owner's error, nullable, may alias comp
+    float* slow[kMaxP];             // UPD kernels only
+    const uint8_t* pc[kMaxP];       // push codes of each rank (the owner's own entry unused)
     const uint32_t* pp[kMaxP];      // push parameters of each rank
     uint8_t* sc;                    // sum codes (message-shaped)
     uint32_t* sp;                   // sum parameters
-    float* err;                     // owner's error, nullable, may alias comp
     int64_t S;
     int64_t tile_begin;
     uint32_t tile_rows;
     int P;
-    int owner;
+    int owner0;
     int negate;
     UpdArgs upd;                    // UPD kernels only
 };
 
-// grid: (ceil(tile_rows / (16 U)), 1).  UPD as for push_kernel.  The peer
-// loop is unrolled to kMaxP with uniform guards on the runtime P.
+// grid: (ceil(tile_rows / (16 U)), owners).  UPD as for push_kernel.  The
+// peer loop is unrolled to kMaxP with uniform guards on the runtime P.
 //
 // LDS is dynamic: the launcher sizes it (at least Io::kLdsFloats floats
 // whenever an fp32 stream is staged), which also sets how many blocks share a
@@ -645,10 +658,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = lane & 15u;
     const uint32_t rw = lane >> 4;
-    const int64_t seg0 = (int64_t)a.owner * a.S + a.tile_begin;
+    const uint32_t y = blockIdx.y;
+    const int owner = a.owner0 + (int)y;
+    const int64_t seg0 = (int64_t)owner * a.S + a.tile_begin;
     const uint32_t last = a.tile_rows - 1u;
-    const bool has_comp = UPD || a.comp != nullptr;
-    const bool has_out = UPD || a.err != nullptr;
+    const uint16_t* const x = a.x[y];
+    float* const comp = (float*)a.comp[y];
+    float* const slow = a.slow[y];
+    float* const err = a.err[y];
+    const bool has_comp = UPD || comp != nullptr;
+    const bool has_out = UPD || err != nullptr;
 
     WaveMap wm[U];
     u32x4 xv[U];
@@ -662,11 +681,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
         wm[k].last = last;
         wm[k].lane = lane;
         const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
-        xv[k] = ld_stream((const u32x4*)(a.x + e0));
-        if (has_comp) io.load(k, wm[k], a.comp, a.upd.slow);
+        xv[k] = ld_stream((const u32x4*)(x + e0));
+        if (has_comp) io.load(k, wm[k], comp, slow);
 #pragma unroll
         for (int j = 0; j < kMaxP; ++j) {
-            if (j < a.P && j != a.owner) {
+            if (j < a.P && j != owner) {
                 pk[k][j].load(a.pc[j], e0);
                 pw[k][j] = a.pp[j][e0 / GROUP];
             }
@@ -691,7 +710,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
 #pragma unroll
         for (int j = 0; j < kMaxP; ++j) {
             if (j >= a.P) break;
-            if (j == a.owner) {
+            if (j == owner) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? own[i] : acc[i] + own[i];
             } else {
@@ -717,24 +736,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
             io.put(lds, k, 0, wave, lane, e);
         }
     }
-    if (has_out) io.flush(lds, wave, lane, wm, UPD ? (float*)a.comp : a.err, a.upd.slow);
+    if (has_out) io.flush(lds, wave, lane, wm, UPD ? comp : err, slow);
 }
 
 // ------------------------------------------------------ gather / tail decode --
 
+// One launch serves one rank or several: blockIdx.z picks the output.
 struct GatherArgs {
     const uint8_t* sc;
     const uint32_t* sp;
-    void* out;
+    void* out[kMaxP];
     int64_t S;
     int64_t tile_begin;
     uint32_t tile_rows;
 };
 
-// grid: (ceil(tile_rows / (16 U)), P); blockIdx.y = segment.  bf16 output
-// is already lane-contiguous (16 B per lane, 1 KB per wave); fp32 output (32 B
-// per lane) goes through the wave's LDS slice like the fp32 streams of push
-// and reduce, so that each store instruction writes 1 KB contiguously.
+// grid: (ceil(tile_rows / (16 U)), P, ranks); blockIdx.y = segment.  bf16
+// output is already lane-contiguous (16 B per lane, 1 KB per wave); fp32
+// output (32 B per lane) goes through the wave's LDS slice like the fp32
+// streams of push and reduce, so that each store instruction writes 1 KB
+// contiguously.
 template <int BITS, bool OUT_BF16, int U, int GROUP>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 {
@@ -745,6 +766,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
     const uint32_t row = threadIdx.x >> 4;
     const int64_t seg0 = (int64_t)blockIdx.y * a.S + a.tile_begin;
     const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
+    void* const out = a.out[blockIdx.z];
 
     Packed<BITS> pk[U];
     uint32_t pw[U];
@@ -769,7 +791,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
             w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
             w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
             w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
-            st_stream((u32x4*)((uint16_t*)a.out + e0), w);
+            st_stream((u32x4*)((uint16_t*)out + e0), w);
         } else {
             natural_write(lds + (k * (kBlock / 64) + wave) * kWaveChunk, lane, v);
         }
@@ -788,7 +810,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 #pragma unroll
             for (uint32_t h = 0; h < 2; ++h) {
                 if (!wm.contig_active(h)) continue;
-                st_stream((f32x4*)((float*)a.out + wm.contig(h)), *(const f32x4*)(sl + 256 * h + 4 * lane));
+                st_stream((f32x4*)((float*)out + wm.contig(h)), *(const f32x4*)(sl + 256 * h + 4 * lane));
             }
         }
     }
@@ -799,8 +821,9 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 struct CompArgs {
     const float* err;
     float* comp;
+    float* slow;        // nullable (beta == 0)
     int64_t n;
-    UpdArgs upd;        // upd.slow nullable (beta == 0)
+    UpdArgs upd;
 };
 
 // grid-stride over float4 chunks, then a scalar tail.  Without a slow memory
@@ -814,13 +837,13 @@ __global__ __launch_bounds__(kBlock) void compensate_kernel(const CompArgs a)
         const f32x4 e = ld_stream((const f32x4*)(a.err + 4 * i));
         float c[4];
         if (SLOW) {
-            const f32x4 m = ld_stream((const f32x4*)(a.upd.slow + 4 * i));
+            const f32x4 m = ld_stream((const f32x4*)(a.slow + 4 * i));
             float mo[4];
             update1(a.upd, e.x, m.x, c[0], mo[0]);
             update1(a.upd, e.y, m.y, c[1], mo[1]);
             update1(a.upd, e.z, m.z, c[2], mo[2]);
             update1(a.upd, e.w, m.w, c[3], mo[3]);
-            st_stream((f32x4*)(a.upd.slow + 4 * i), f32x4{mo[0], mo[1], mo[2], mo[3]});
+            st_stream((f32x4*)(a.slow + 4 * i), f32x4{mo[0], mo[1], mo[2], mo[3]});
         } else {
             c[0] = -(a.upd.alpha * e.x); c[1] = -(a.upd.alpha * e.y);
             c[2] = -(a.upd.alpha * e.z); c[3] = -(a.upd.alpha * e.w);
@@ -833,8 +856,8 @@ __global__ __launch_bounds__(kBlock) void compensate_kernel(const CompArgs a)
             const float e = a.err[i];
             if (SLOW) {
                 float c, mo;
-                update1(a.upd, e, a.upd.slow[i], c, mo);
-                a.upd.slow[i] = mo;
+                update1(a.upd, e, a.slow[i], c, mo);
+                a.slow[i] = mo;
                 a.comp[i] = c;
             } else {
                 a.comp[i] = -(a.upd.alpha * e);
