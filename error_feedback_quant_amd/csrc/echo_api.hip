@@ -285,6 +285,36 @@ SimLayout sim_layout(int P, int64_t n, int bits, int group)
     return L;
 }
 
+// ------------------------------------------------------------ static scratch --
+// The allocation-free call keeps the push and sum codes in this array.  In
+// host code `scratch` names a host-side stand-in, not device memory: kernels
+// get the device address that hipGetSymbolAddress returns, taken once per
+// device (each device holds its own copy of the array until the process ends).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_device(uint8_t** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return ECHO_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!p) return ECHO_EHIP;
+        g_scratch_ptr[dev] = (uint8_t*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ECHO_OK;
+}
+
 }  // namespace
 
 // ======================================================================= ABI
@@ -300,6 +330,7 @@ const char* echo_status_str(int status)
     case ECHO_EUNSUP: return "unsupported bits, group or output dtype";
     case ECHO_ESHAPE: return "invalid message or tile shape";
     case ECHO_EHIP: return "HIP runtime error";
+    case ECHO_ETOOBIG: return "message needs more workspace than the static scratch of the allocation-free call";
     default: return "unknown status";
     }
 }
@@ -439,7 +470,14 @@ size_t echo_allreduce_sim_workspace_bytes(int P, int64_t n, int bits, int group)
     return sim_layout(P, n, bits, group).total;
 }
 
-int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstreams)
+}  // extern "C"
+
+namespace {
+
+// The whole simulated call.  With noalloc the push and sum codes live in the
+// static scratch array of this device (a->workspace is ignored) and every
+// stage runs on the first stream, so the call creates no events either.
+int sim_impl(const echo_sim_args* a, void* const* streams, int nstreams, bool noalloc)
 {
     if (!a) return ECHO_EINVAL;
     const int P = a->P;
@@ -480,11 +518,18 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
             return ECHO_EALIGN;
     }
     const SimLayout L = sim_layout(P, n, a->bits, a->group);
-    if (!a->workspace || a->workspace_bytes < L.total) return ECHO_EINVAL;
-    if (!aligned16(a->workspace)) return ECHO_EALIGN;
+    uint8_t* ws = nullptr;
+    if (noalloc) {
+        if (L.total > kScratchBytes) return ECHO_ETOOBIG;
+        if ((rc = scratch_on_device(&ws))) return rc;
+        nstreams = 1;
+    } else {
+        if (!a->workspace || a->workspace_bytes < L.total) return ECHO_EINVAL;
+        if (!aligned16(a->workspace)) return ECHO_EALIGN;
+        ws = (uint8_t*)a->workspace;
+    }
 
     // workspace: push codes of every rank, push params of every rank, sum codes, sum params
-    uint8_t* ws = (uint8_t*)a->workspace;
     const uint8_t* pc[ECHO_MAX_P];
     const echo_qparam* pp[ECHO_MAX_P];
     for (int r = 0; r < P; ++r) {
@@ -620,5 +665,22 @@ int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstream
     }
     return ECHO_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int echo_allreduce_sim(const echo_sim_args* a, void* const* streams, int nstreams)
+{
+    return sim_impl(a, streams, nstreams, false);
+}
+
+int echo_allreduce_sim_noalloc(const echo_sim_args* a, void* stream)
+{
+    void* st[1] = {stream};
+    return sim_impl(a, st, 1, true);
+}
+
+size_t echo_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-OK, EINVAL, EALIGN, EUNSUP, ESHAPE, EHIP = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, EUNSUP, ESHAPE, EHIP, ETOOBIG = 0, -1, -2, -3, -4, -5, -6
 OUT_F32, OUT_BF16 = 0, 1
 ERR_NEGATED = 1
 QUANT_NAIVE, QUANT_SYMMETRIC = 2, 4
@@ -79,6 +79,10 @@ _lib.echo_allreduce_sim_workspace_bytes.restype = c_size_t
 _lib.echo_allreduce_sim_workspace_bytes.argtypes = [c_int, c_int64, c_int, c_int]
 _lib.echo_allreduce_sim.restype = c_int
 _lib.echo_allreduce_sim.argtypes = [POINTER(SimArgs), c_void_p, c_int]
+_lib.echo_allreduce_sim_noalloc.restype = c_int
+_lib.echo_allreduce_sim_noalloc.argtypes = [POINTER(SimArgs), c_void_p]
+_lib.echo_noalloc_scratch_bytes.restype = c_size_t
+_lib.echo_noalloc_scratch_bytes.argtypes = []
 
 
 def lib():
@@ -182,3 +186,13 @@ def echo_allreduce_sim(args: SimArgs, streams=None):
     else:
         arr, ns = (c_void_p * len(streams))(*[_stream(s) for s in streams]), len(streams)
     _check("echo_allreduce_sim", _lib.echo_allreduce_sim(ctypes.byref(args), arr, ns))
+
+
+def echo_allreduce_sim_noalloc(args: SimArgs, stream=None):
+    """The allocation-free call: args.workspace is ignored; every stage runs
+    on `stream` (a torch stream or handle; None = torch's current stream)."""
+    _check("echo_allreduce_sim_noalloc", _lib.echo_allreduce_sim_noalloc(ctypes.byref(args), _stream(stream)))
+
+
+def echo_noalloc_scratch_bytes() -> int:
+    return int(_lib.echo_noalloc_scratch_bytes())

@@ -65,7 +65,9 @@ enum echo_status {
     ECHO_EALIGN = -2, /* a data pointer is not 16-byte aligned */
     ECHO_EUNSUP = -3, /* bits not 4/8, group not 128/256, unknown output dtype */
     ECHO_ESHAPE = -4, /* n or tile not a valid multiple / out of range */
-    ECHO_EHIP = -5    /* a HIP launch or runtime call failed; see echo_last_hip_error */
+    ECHO_EHIP = -5,   /* a HIP launch or runtime call failed; see echo_last_hip_error */
+    ECHO_ETOOBIG = -6 /* echo_allreduce_sim_noalloc: the message needs more workspace than
+                         echo_noalloc_scratch_bytes() */
 };
 
 enum echo_out_dtype { ECHO_OUT_F32 = 0, ECHO_OUT_BF16 = 1 };
@@ -294,6 +296,32 @@ size_t echo_allreduce_sim_workspace_bytes(int P, int64_t n, int bits, int group)
 
 /* streams: host array of nstreams hipStream_t handles, or NULL. */
 int echo_allreduce_sim(const echo_sim_args* args, void* const* streams, int nstreams);
+
+/*
+ * echo_allreduce_sim_noalloc — echo_allreduce_sim for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: the push and sum
+ * codes go to a static device array of echo_noalloc_scratch_bytes() bytes
+ * (64 MiB) that the library holds on every device it runs on until the
+ * process ends; args->workspace and args->workspace_bytes are ignored.  Every
+ * stage runs on `stream` (hipStream_t, NULL = the null stream), tile after
+ * tile, so no events are created either; results are those of
+ * echo_allreduce_sim, bit for bit.  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.
+ *
+ * Errors: those of echo_allreduce_sim (except the workspace checks), and
+ * ECHO_ETOOBIG, with nothing enqueued, when
+ * echo_allreduce_sim_workspace_bytes(P, n, bits, group) exceeds the array:
+ * at 4-bit codes and g = 128 that is n above about 25 million elements per
+ * rank for P = 4.  Calls on one device share the array: calls that overlap
+ * in time on one device race and must be ordered by the caller (for example
+ * by issuing them on one stream).  Nothing in the array needs clearing
+ * between calls: every byte a call reads was written earlier in that call.
+ */
+int echo_allreduce_sim_noalloc(const echo_sim_args* args, void* stream);
+
+/* Size in bytes of the static scratch array of echo_allreduce_sim_noalloc. */
+size_t echo_noalloc_scratch_bytes(void);
 
 /* Static description of a status code. */
 const char* echo_status_str(int status);

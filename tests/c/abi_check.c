@@ -68,6 +68,11 @@ int main(void)
     expect("sim tiles 0", echo_allreduce_sim(&a, NULL, 0), ECHO_EINVAL);
     a.tiles = 1; a.n = 0;
     expect("sim empty", echo_allreduce_sim(&a, NULL, 0), ECHO_OK);
+    expect("noalloc scratch", (int)(echo_noalloc_scratch_bytes() == ((size_t)64 << 20)), 1);
+    expect("noalloc null args", echo_allreduce_sim_noalloc(NULL, NULL), ECHO_EINVAL);
+    a.n = (int64_t)1 << 25;
+    for (int r = 0; r < 4; ++r) { a.x[r] = x; a.out[r] = fake; }
+    expect("noalloc too big", echo_allreduce_sim_noalloc(&a, NULL), ECHO_ETOOBIG);
     expect("last hip error", echo_last_hip_error(), 0);
 
     printf(fails ? "abi_check: %d failures\n" : "abi_check: ok\n", fails);

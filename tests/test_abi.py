@@ -12,6 +12,7 @@ def test_every_declared_function_is_exported():
     names = echo.declared_functions()
     expected = {"echo_quantize_ef", "echo_reduce_segment", "echo_gather_dequant", "echo_compensate",
                 "echo_gemm_quantize_ef", "echo_allreduce_sim", "echo_allreduce_sim_workspace_bytes",
+                "echo_allreduce_sim_noalloc", "echo_noalloc_scratch_bytes",
                 "echo_status_str", "echo_last_hip_error"}
     assert expected <= set(names), names
     L = echo.lib()
@@ -21,8 +22,8 @@ def test_every_declared_function_is_exported():
 
 def test_status_strings():
     L = echo.lib()
-    for rc in (0, -1, -2, -3, -4, -5):
-        assert L.echo_status_str(rc)
+    for rc in (0, -1, -2, -3, -4, -5, -6):
+        assert L.echo_status_str(rc) != b"unknown status"
     assert L.echo_status_str(123) == b"unknown status"
     assert L.echo_last_hip_error() == 0
 
@@ -167,3 +168,36 @@ def test_header_is_plain_c_and_links(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_check: ok" in r.stdout
+
+
+def test_noalloc_argument_checks():
+    """The allocation-free call checks its arguments like echo_allreduce_sim
+    (minus the workspace) and rejects a message whose workspace exceeds the
+    static scratch before it touches the device."""
+    P = 4
+    limit = echo.echo_noalloc_scratch_bytes()
+    assert limit == 64 << 20
+
+    def sim(n, **kw):
+        a = echo.SimArgs()
+        a.P, a.bits, a.group, a.tiles, a.out_dtype, a.ef = P, 4, 128, 1, 1, 0
+        a.alpha, a.beta, a.n = 1.0, 0.0, n
+        for r in range(P):
+            a.x[r] = FAKE
+            a.out[r] = FAKE
+        for k, v in kw.items():
+            if k in ("x", "out", "comp"):
+                for r, p in enumerate(v):
+                    getattr(a, k)[r] = p
+            else:
+                setattr(a, k, v)
+        return rc_of(echo.echo_allreduce_sim_noalloc, a, stream=0)
+
+    n_big = 1 << 25
+    assert echo.echo_allreduce_sim_workspace_bytes(P, n_big, 4) > limit
+    assert sim(n_big) == echo.ETOOBIG
+    assert sim(n_big, tiles=0) == echo.EINVAL
+    assert sim(n_big, x=[FAKE, None, FAKE, FAKE]) == echo.EINVAL
+    assert sim(n_big, out=[FAKE + 2, FAKE, FAKE, FAKE]) == echo.EALIGN
+    assert sim(n_big, ef=1) == echo.EINVAL                  # comp missing
+    assert sim(0) == 0                                      # empty message: nothing to do

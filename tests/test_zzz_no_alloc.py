@@ -1,0 +1,74 @@
+"""GPU check of echo_allreduce_sim_noalloc, the allocation-free variant of
+echo_allreduce_sim for callers that cannot allocate device memory: through the
+C ABI, its outputs and compensation equal those of echo_allreduce_sim (bit for
+bit) on two calls in a row, the second with a smaller message (the static
+scratch keeps the first call's contents), with tiles; and a message whose
+workspace exceeds the static scratch is rejected with nothing enqueued."""
+import numpy as np
+import pytest
+import torch
+
+from _helpers import DEV, assert_bits_equal, dev_u16, host_f32, host_u16, rand_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def echo():
+    from error_feedback_quant_amd import echo as e
+    assert torch.cuda.is_available()
+    return e
+
+
+def run_pair(echo, P, n, bits, tiles, seed):
+    """The same call through both entry points, each with its own state."""
+    xs = [dev_u16(rand_bf16(n, seed + r)) for r in range(P)]
+    got = {}
+    for which in ("noalloc", "workspace"):
+        comps = [torch.full((n,), 0.0, dtype=torch.float32, device=DEV) for _ in range(P)]
+        outs = [torch.full((n,), 0x3F3F, dtype=torch.int16, device=DEV) for _ in range(P)]
+        if which == "noalloc":
+            a = echo.make_sim_args(xs, outs, None, bits=bits, tiles=tiles, out_dtype=echo.OUT_BF16, ef=True,
+                                   comps=comps, workspace_bytes=0)
+            for _ in range(2):                      # the compensation carries into the second call
+                echo.echo_allreduce_sim_noalloc(a)
+        else:
+            ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits), dtype=torch.uint8, device=DEV)
+            a = echo.make_sim_args(xs, outs, ws, bits=bits, tiles=tiles, out_dtype=echo.OUT_BF16, ef=True,
+                                   comps=comps)
+            streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+            for _ in range(2):
+                echo.echo_allreduce_sim(a, streams=streams)
+        torch.cuda.synchronize()
+        got[which] = ([host_u16(o) for o in outs], [host_f32(c) for c in comps])
+    for r in range(P):
+        assert_bits_equal(got["noalloc"][0][r], got["workspace"][0][r], f"out rank {r}")
+        assert_bits_equal(got["noalloc"][1][r], got["workspace"][1][r], f"comp rank {r}")
+
+
+def test_noalloc_equals_workspace_call_twice_smaller_second(echo):
+    limit = echo.echo_noalloc_scratch_bytes()
+    assert limit == 64 << 20
+    say("noalloc", "P=4 n=2^22+512 bits=4 tiles=3")
+    n1 = (1 << 22) + 512
+    assert echo.echo_allreduce_sim_workspace_bytes(4, n1, 4) <= limit
+    run_pair(echo, 4, n1, 4, 3, 100)
+    say("noalloc", "P=8 n=2^17 bits=8 tiles=1 (smaller, after the first)")
+    run_pair(echo, 8, 1 << 17, 8, 1, 200)
+
+
+def test_noalloc_rejects_a_message_beyond_the_scratch(echo):
+    P, bits = 4, 4
+    limit = echo.echo_noalloc_scratch_bytes()
+    n = 1 << 25                                    # 85 MB of workspace at P = 4
+    assert echo.echo_allreduce_sim_workspace_bytes(P, n, bits) > limit
+    say("noalloc reject", P, n)
+    xs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    outs = [torch.full((n,), 0x3F3F, dtype=torch.int16, device=DEV) for _ in range(P)]
+    a = echo.make_sim_args(xs, outs, None, bits=bits, tiles=1, out_dtype=echo.OUT_BF16, workspace_bytes=0)
+    with pytest.raises(echo.EchoError) as ei:
+        echo.echo_allreduce_sim_noalloc(a)
+    assert ei.value.rc == echo.ETOOBIG
+    torch.cuda.synchronize()
+    for o in outs:
+        assert bool((o == 0x3F3F).all())           # nothing was enqueued
