@@ -40,7 +40,8 @@ OK, EINVAL, EUNSUP, ESHAPE = 0, -1, -3, -4
 ERR_NEGATED = 1
 Q_NAIVE, Q_SYMMETRIC = 2, 4          # quantizer flag bits (Table 8 ablations)
 X_ALL = 8                            # gemm_quantize_ef: x_out receives every segment
-QUANTS = {"zero_aware": 0, "naive": Q_NAIVE, "symmetric": Q_SYMMETRIC}
+Q_MSE = 16                           # quantizer flag bit: zero point searched for the least squared error
+QUANTS = {"zero_aware": 0, "naive": Q_NAIVE, "symmetric": Q_SYMMETRIC, "mse": Q_MSE}
 OUT_F32, OUT_BF16 = 0, 1
 
 CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fexcess-precision=standard",
@@ -165,12 +166,12 @@ def f16_bits_to_f32(h: int) -> float:
 
 def quantize_group(v, bits: int, quant: str = "zero_aware"):
     """Q_b of one group with the named quantizer ("zero_aware", "naive",
-    "symmetric").  Returns (codes uint8 [g], scale_bits, zero_bits)."""
+    "symmetric", "mse").  Returns (codes uint8 [g], scale_bits, zero_bits)."""
     v = np.ascontiguousarray(v, dtype=np.float32)
     q = np.zeros(v.size, dtype=np.uint8)
     sh = ctypes.c_uint16()
     zh = ctypes.c_uint16()
-    mode = {"zero_aware": 0, "naive": 1, "symmetric": 2}[quant]
+    mode = {"zero_aware": 0, "naive": 1, "symmetric": 2, "mse": 3}[quant]
     _check("quantize_group", lib().echo_ref_quantize_group_q(_p(v), v.size, bits, mode, _p(q),
                                                              ctypes.byref(sh), ctypes.byref(zh)))
     return q, int(sh.value), int(zh.value)

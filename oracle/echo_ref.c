@@ -57,15 +57,16 @@
 #define REF_ERR_NEGATED 1   /* write -e (the next call's compensation) instead of e */
 #define REF_Q_NAIVE 2       /* quantizer: naive zero point (Table 8 ablation)          */
 #define REF_Q_SYMMETRIC 4   /* quantizer: symmetric grid (Table 8 ablation)            */
+#define REF_Q_MSE 16        /* quantizer: zero point searched for the least squared error */
 
-enum { Q_ZERO_AWARE = 0, Q_NAIVE = 1, Q_SYMMETRIC = 2 };
+enum { Q_ZERO_AWARE = 0, Q_NAIVE = 1, Q_SYMMETRIC = 2, Q_MSE = 3 };
 
-/* quantizer selected by the flag bits; -1 when both ablations are asked for */
+/* quantizer selected by the flag bits; -1 when more than one is asked for */
 static int quant_of(int flags)
 {
-    int naive = (flags & REF_Q_NAIVE) != 0, sym = (flags & REF_Q_SYMMETRIC) != 0;
-    if (naive && sym) return -1;
-    return naive ? Q_NAIVE : (sym ? Q_SYMMETRIC : Q_ZERO_AWARE);
+    int naive = (flags & REF_Q_NAIVE) != 0, sym = (flags & REF_Q_SYMMETRIC) != 0, mse = (flags & REF_Q_MSE) != 0;
+    if (naive + sym + mse > 1) return -1;
+    return naive ? Q_NAIVE : (sym ? Q_SYMMETRIC : (mse ? Q_MSE : Q_ZERO_AWARE));
 }
 #define REF_OUT_F32 0
 #define REF_OUT_BF16 1
@@ -272,8 +273,66 @@ static void quant_symmetric(const float* v, int g, int bits, uint8_t* q, uint16_
     *scale_h = sh;
 }
 
+/* Zero point searched for the least squared error (a variant of the full
+ * method: Table 8 names the zero-aware quantizer's zero point as the part
+ * that matters; this variant keeps the full method's scale and replaces the
+ * closed-form zero point by an exhaustive search).  Reading: the scale s,
+ * 1/s and the codes' rule are those of the zero-aware quantizer; the zero
+ * point is the integer z in [0, Qm] whose codes
+ *   q_i(z) = clamp(rint(t_i) + z, 0, Qm),   t_i = v_i * (1/s)  (fp32 product)
+ * give the least squared error of the group measured in units of s,
+ *   E(z) = sum_i (q_i(z) - z - t_i)^2,
+ * the smallest such z when several tie.  z only moves codes through the
+ * clamp: with r_i = rint(t_i) and c_i = clamp(r_i, -z, Qm - z) = q_i(z) - z,
+ *   E(z) = sum_i (r_i - t_i)^2 + D(z),   D(z) = sum_i (c_i - r_i)(c_i + r_i - 2 t_i),
+ * and the first sum does not depend on z, so the search compares D(z).
+ * D is evaluated exactly in double: a term is nonzero only for a clamped
+ * element, whose |t_i| >= 1/2 makes t_i a multiple of 2^-24 below 2^10 in
+ * magnitude, so every term is a multiple of 2^-24 below 2^19 and every
+ * partial sum of at most 256 of them has fewer than 53 significant bits.
+ * An all-zero group gives s = +0, z = 0, codes 0.
+ * Pinned by: the exact squared error of every z computed with rationals on
+ * tiny groups (smallest argmin), the scale of the full method, and never a
+ * larger error than the closed-form zero point. */
+static void quant_mse(const float* v, int g, int Qm, uint8_t* q, uint16_t* scale_h, uint16_t* zero_h)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int i = 0; i < g; ++i) {
+        if (v[i] < lo) lo = v[i];
+        if (v[i] > hi) hi = v[i];
+    }
+    if (hi == lo) {
+        for (int i = 0; i < g; ++i) q[i] = 0;
+        *scale_h = 0;
+        *zero_h = 0;
+        return;
+    }
+    uint16_t sh = scale_bits((hi - lo) / (float)Qm);
+    float s = echo_ref_f16_to_f32(sh);
+    float inv = 1.0f / s;
+    int best_z = 0;
+    double best = 0.0;
+    for (int z = 0; z <= Qm; ++z) {
+        double d = 0.0;
+        for (int i = 0; i < g; ++i) {
+            float t = v[i] * inv;
+            double r = (double)rintf(t);
+            double c = r < (double)-z ? (double)-z : (r > (double)(Qm - z) ? (double)(Qm - z) : r);
+            d += (c - r) * (c + r - 2.0 * (double)t);
+        }
+        if (z == 0 || d < best) {
+            best = d;
+            best_z = z;
+        }
+    }
+    for (int i = 0; i < g; ++i) q[i] = clamp_code((double)rintf(v[i] * inv) + (double)best_z, Qm);
+    *scale_h = sh;
+    *zero_h = echo_ref_f32_to_f16((float)best_z);
+}
+
 /* Quantize one group of g values to unsigned b-bit codes (one per byte in q)
- * with quantizer `quant` (0 zero-aware, 1 naive zero point, 2 symmetric). */
+ * with quantizer `quant` (0 zero-aware, 1 naive zero point, 2 symmetric,
+ * 3 zero point searched for the least squared error). */
 int echo_ref_quantize_group_q(const float* v, int g, int bits, int quant, uint8_t* q,
                               uint16_t* scale_h, uint16_t* zero_h)
 {
@@ -284,6 +343,7 @@ int echo_ref_quantize_group_q(const float* v, int g, int bits, int quant, uint8_
     case Q_ZERO_AWARE: quant_zero_aware(v, g, Qm, q, scale_h, zero_h); return REF_OK;
     case Q_NAIVE: quant_naive(v, g, Qm, q, scale_h, zero_h); return REF_OK;
     case Q_SYMMETRIC: quant_symmetric(v, g, bits, q, scale_h, zero_h); return REF_OK;
+    case Q_MSE: quant_mse(v, g, Qm, q, scale_h, zero_h); return REF_OK;
     default: return REF_EINVAL;
     }
 }
@@ -562,7 +622,7 @@ int echo_ref_compensate(const float* err, float* comp_next, float* slow, int64_t
 /* and echo_ref_compensate turns it into comp (and slow).  For the classic   */
 /* update (alpha = 1, beta = 0) with err NULL, -e is written straight into  */
 /* comp, identical to computing e and then c' = -(1*e).                     */
-/* qflags selects the quantizer (0, REF_Q_NAIVE or REF_Q_SYMMETRIC).        */
+/* qflags selects the quantizer (0, REF_Q_NAIVE, REF_Q_SYMMETRIC, REF_Q_MSE). */
 /* Instrumentation ([EchoCard] abstract and Fig. 2: at most two              */
 /* quantizations per element per call), filled from counters that the push  */
 /* and reduce loops above increment as they run:                             */
@@ -577,7 +637,7 @@ int echo_ref_allreduce(int P, int64_t n, int bits, int g, int ef, float alpha, f
                        float* const* err, void* const* out, int out_dtype,
                        int* qdepth, int64_t* qwork, int qflags)
 {
-    if (quant_of(qflags) < 0 || (qflags & ~(REF_Q_NAIVE | REF_Q_SYMMETRIC))) return REF_EINVAL;
+    if (quant_of(qflags) < 0 || (qflags & ~(REF_Q_NAIVE | REF_Q_SYMMETRIC | REF_Q_MSE))) return REF_EINVAL;
     int rc = check_shape(n, P, 0, 0, bits, g);
     if (rc) return rc;
     if (out_dtype != REF_OUT_F32 && out_dtype != REF_OUT_BF16) return REF_EUNSUP;

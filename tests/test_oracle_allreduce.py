@@ -442,7 +442,8 @@ def test_wire_bytes_per_pushed_element(bits, ratio):
         assert 3.5 < 16 / bits_per_elem < 4.0        # almost four times fewer bytes
 
 
-@pytest.mark.parametrize("quant,group", [("naive", 128), ("symmetric", 128), ("zero_aware", 256)])
+@pytest.mark.parametrize("quant,group", [("naive", 128), ("symmetric", 128), ("zero_aware", 256), ("mse", 128),
+                                         ("mse", 256)])
 def test_chunked_calls_equal_one_whole_call_variants(quant, group):
     """The chunked form of the oracle's call (as the full-size GPU parity runs
     it) for Table 8's quantizers and groups of 256: equal to one whole call,

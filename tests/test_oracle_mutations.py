@@ -11,7 +11,8 @@ The mistakes are the ones a reader of the Echo paper card (Table 8, Fig. 2(a),
 appendix Fig. 4) and of the PhantomByte article ("The cancellation rule")
 could plausibly make when writing the oracle: in the quantizer (tie rule,
 side of the zero-point add, range not widened to 0, 2^b levels instead of
-2^b - 1, codes measured from the range start), in the call structure (wrong
+2^b - 1, codes measured from the range start), in the zero-point search
+(tie rule, objective without the rounding part), in the call structure (wrong
 segment pushed, owner's term or compensation dropped or taken from a peer,
 summation order), in the compensator (sign, slow-memory input), in decoding
 and packing (off-by-one, nibble order, neighbouring group's parameters), in
@@ -106,6 +107,12 @@ MUTATIONS = [
     ("bfloat16 output truncated",
      [("if (rem > 0x8000u || (rem == 0x8000u && (up & 1u))) up += 1u;", "(void)rem;", 0)],
      [FM + "test_bf16_round_to_nearest_even_matches_torch"]),
+    ("zero-point search keeps the larger zero point on ties",
+     [("if (z == 0 || d < best) {", "if (z == 0 || d <= best) {", 0)],
+     ["tests/test_oracle_quantizer_mse.py::test_hand_worked_tie_takes_the_smaller_zero_point"]),
+    ("zero-point search scores the clamped codes without the rounding part",
+     [("d += (c - r) * (c + r - 2.0 * (double)t);", "d += (c - r) * (c - r);", 0)],
+     ["tests/test_oracle_quantizer_mse.py::test_exhaustive_exact_search_on_tiny_groups"]),
     ("zero binary16 scale not clamped to 2^-24",
      [("if (sh == 0x0000u) sh = 0x0001u;", "if (0) sh = 0x0001u;", 0)],
      [QZ + "test_scale_clamps_and_all_zero_group"]),

@@ -153,7 +153,7 @@ def test_naive_round_trip_and_missing_zero(bits):
     assert misses > 150
 
 
-@pytest.mark.parametrize("quant", ["naive", "symmetric"])
+@pytest.mark.parametrize("quant", ["naive", "symmetric", "mse"])
 @pytest.mark.parametrize("P", [2, 4])
 def test_call_structure_holds_for_every_quantizer(quant, P):
     """Identical outputs, at most two quantizations, and the error identity do
@@ -198,18 +198,19 @@ def test_naive_zero_point_of_a_zero_minimum_is_plus_zero(bits):
 def test_both_ablations_at_once_is_rejected():
     n, P = 4 * 128, 4
     x = np.zeros(n, np.uint16)
-    with pytest.raises(oracle.OracleError):
-        oracle.quantize_ef(x, None, n, P, 0, 0, 128, 4, 128, np.zeros(n, np.uint8),
-                           np.zeros(2 * n // 128, np.uint16), None, oracle.Q_NAIVE | oracle.Q_SYMMETRIC)
+    for flags in (oracle.Q_NAIVE | oracle.Q_SYMMETRIC, oracle.Q_NAIVE | oracle.Q_MSE, oracle.Q_SYMMETRIC | oracle.Q_MSE):
+        with pytest.raises(oracle.OracleError):
+            oracle.quantize_ef(x, None, n, P, 0, 0, 128, 4, 128, np.zeros(n, np.uint8),
+                               np.zeros(2 * n // 128, np.uint16), None, flags)
 
 
-@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric"])
+@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric", "mse"])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_steps_use_the_selected_quantizer(quant, bits):
     """The flag bits reach the group quantizer pinned above: the push step's
     codes and parameters are that quantizer's, group by group, and a one-rank
     call is one round trip through it."""
-    flag = {"zero_aware": 0, "naive": oracle.Q_NAIVE, "symmetric": oracle.Q_SYMMETRIC}[quant]
+    flag = oracle.QUANTS[quant]
     rng = np.random.default_rng(110 + bits)
     P, n, g = 4, 4 * 128 * 2, 128
     x = oracle.f32_to_bf16_bits((rng.standard_normal(n) + 0.7).astype(np.float32))
