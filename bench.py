@@ -41,7 +41,8 @@ Also printed (same JSON line):
                 as independent calls on ranges of every segment in host
                 threads, at P = 4 and 8; with the host's CPU count and model.
   variants      the same call with Table 8's ablation quantizers (naive zero
-                point, symmetric grid) and with groups of 256.
+                point, symmetric grid), with groups of 256, and with the zero
+                point searched for the least squared error.
   modes         the same call with feedback off, with fp32 output, with
                 the two-timescale compensator fused into push and reduce
                 (B then counts 16 bytes of state traffic instead of 8), and
@@ -547,7 +548,7 @@ def main():
     if not a.no_variants:
         variants = {}
         for name, quant, group in (("naive_zero_point", "naive", G), ("symmetric_grid", "symmetric", G),
-                                   ("zero_aware_g256", "zero_aware", 256)):
+                                   ("zero_aware_g256", "zero_aware", 256), ("searched_zero_point", "mse", G)):
             rv = run_case(echo, torch, inputs, a.P, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 3),
                           a.warmup, out_bf16, ef, time_kernel=False, quant=quant, group=group)
             variants[name] = leg(rv)

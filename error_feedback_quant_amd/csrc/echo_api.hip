@@ -84,15 +84,16 @@ unsigned blocks_for(uint32_t tile_rows, int u)
     return (tile_rows + echo::kRowsPerBlock * u - 1) / (echo::kRowsPerBlock * u);
 }
 
-// quantizer selected by the flag bits (-1: both ablations asked for)
+// quantizer selected by the flag bits (-1: more than one asked for)
 int quant_of(int flags)
 {
-    const bool naive = flags & ECHO_QUANT_NAIVE, sym = flags & ECHO_QUANT_SYMMETRIC;
-    if (naive && sym) return -1;
-    return naive ? echo::kNaive : (sym ? echo::kSymmetric : echo::kZeroAware);
+    const bool naive = flags & ECHO_QUANT_NAIVE, sym = flags & ECHO_QUANT_SYMMETRIC, mse = flags & ECHO_QUANT_MSE;
+    if ((int)naive + (int)sym + (int)mse > 1) return -1;
+    return naive ? echo::kNaive : (sym ? echo::kSymmetric : (mse ? echo::kMse : echo::kZeroAware));
 }
 
-constexpr int kKnownFlags = ECHO_ERR_NEGATED | ECHO_QUANT_NAIVE | ECHO_QUANT_SYMMETRIC;
+constexpr int kQuantFlags = ECHO_QUANT_NAIVE | ECHO_QUANT_SYMMETRIC | ECHO_QUANT_MSE;
+constexpr int kKnownFlags = ECHO_ERR_NEGATED | kQuantFlags;
 
 // Runtime (bits, update, quantizer, group) -> kernel template instance.
 template <template <int, bool, int, int> class L, typename A>
@@ -104,6 +105,7 @@ void dispatch(int bits, bool upd, int quant, int group, const A& a, dim3 grid, h
 #define ECHO_D2(B, UP)                                                \
     if (quant == echo::kNaive) { ECHO_D3(B, UP, echo::kNaive) }       \
     else if (quant == echo::kSymmetric) { ECHO_D3(B, UP, echo::kSymmetric) } \
+    else if (quant == echo::kMse) { ECHO_D3(B, UP, echo::kMse) }      \
     else { ECHO_D3(B, UP, echo::kZeroAware) }
 #define ECHO_D1(B)                                                    \
     if (upd) { ECHO_D2(B, true) } else { ECHO_D2(B, false) }
@@ -395,10 +397,12 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
     if (bits == 4) {
         if (q == echo::kZeroAware) ECHO_GEMM_GO(4, echo::kZeroAware);
         else if (q == echo::kNaive) ECHO_GEMM_GO(4, echo::kNaive);
+        else if (q == echo::kMse) ECHO_GEMM_GO(4, echo::kMse);
         else ECHO_GEMM_GO(4, echo::kSymmetric);
     } else {
         if (q == echo::kZeroAware) ECHO_GEMM_GO(8, echo::kZeroAware);
         else if (q == echo::kNaive) ECHO_GEMM_GO(8, echo::kNaive);
+        else if (q == echo::kMse) ECHO_GEMM_GO(8, echo::kMse);
         else ECHO_GEMM_GO(8, echo::kSymmetric);
     }
 #undef ECHO_GEMM_GO
@@ -486,7 +490,7 @@ int sim_impl(const echo_sim_args* a, void* const* streams, int nstreams, bool no
     if (a->out_dtype != ECHO_OUT_F32 && a->out_dtype != ECHO_OUT_BF16) return ECHO_EUNSUP;
     if (a->tiles < 1) return ECHO_EINVAL;
     if (a->ef != 0 && a->ef != 1) return ECHO_EINVAL;
-    if ((a->quant & ~(ECHO_QUANT_NAIVE | ECHO_QUANT_SYMMETRIC)) || quant_of(a->quant) < 0) return ECHO_EINVAL;
+    if ((a->quant & ~kQuantFlags) || quant_of(a->quant) < 0) return ECHO_EINVAL;
     if (streams && nstreams < 1) return ECHO_EINVAL;
     const int64_t n = a->n;
     if (n == 0) return ECHO_OK;

@@ -44,8 +44,9 @@ constexpr int kBlock = 256;                    // 4 wavefronts of 64
 constexpr int kRowsPerBlock = kBlock / kRowLanes;  // 16 rows per pass
 constexpr int kMaxP = 8;
 
-// quantizers (Table 8): the full method and its two ablations
-enum Quant { kZeroAware = 0, kNaive = 1, kSymmetric = 2 };
+// quantizers (Table 8): the full method, its two ablations, and the full
+// method with its zero point searched for the least squared error
+enum Quant { kZeroAware = 0, kNaive = 1, kSymmetric = 2, kMse = 3 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -182,7 +183,7 @@ struct QParams {
 template <int QUANT>
 __device__ __forceinline__ void lane_stats(const float* u, float& lo, float& hi)
 {
-    if constexpr (QUANT == kZeroAware) {
+    if constexpr (QUANT == kZeroAware || QUANT == kMse) {
         lo = 0.0f; hi = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) { lo = fminf(lo, u[i]); hi = fmaxf(hi, u[i]); }
@@ -222,7 +223,7 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
 {
     constexpr float kQm = (float)((1 << BITS) - 1);
     QParams p;
-    if constexpr (QUANT == kZeroAware) {
+    if constexpr (QUANT == kZeroAware || QUANT == kMse) {
         // range holds 0; integer zero point, so 0 is exactly code z
         const uint32_t sb = scale_bits(div_by_const<(1 << BITS) - 1>(hi - lo));
         const float s = f16_bits_to_f32(sb);
@@ -374,6 +375,86 @@ __device__ __forceinline__ void decode8_q(const float* q, uint32_t word, float* 
     }
 }
 
+// ------------------------------------------------------ zero-point search --
+// The zero point of the kMse quantizer: the z in [0, Qm] that minimizes the
+// group's squared error in units of s, sum_i (clamp(r_i + z, 0, Qm) - z - t_i)^2
+// with t_i = u_i * (1/s) and r_i = rint(t_i) as the codes use them, the
+// smallest z on ties.  z moves codes only through the clamp, so the search
+// compares D(z) = sum_i (c_i - r_i)(c_i + r_i - 2 t_i), c_i = clamp(r_i, -z,
+// Qm - z), which differs from the squared error by a constant.  A term is
+// nonzero only for a clamped element, whose |t_i| >= 1/2 makes it a multiple
+// of 2^-24 below 2^19 in magnitude; in fp64 every term and every partial sum
+// is exact, so the cross-lane sum cannot depend on its order.  D is convex
+// in z (every term is 0 on an interval and a convex quadratic outside it),
+// so a descent from the closed-form zero point reaches the smallest
+// minimizer: down while D does not increase, else up while D decreases.
+
+// sum over the lanes of a group (16 lanes, or 32 for GROUP = 256) of an exact fp64 value
+template <int GROUP>
+__device__ __forceinline__ double group_sum_f64(double d)
+{
+    auto step = [&](auto mov) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, d);
+        const int lo = mov((int)(uint32_t)b), hi = mov((int)(uint32_t)(b >> 32));
+        d += __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    };
+    step([](int v) { return dpp_i<0xB1>(v); });    // quad_perm [1,0,3,2]
+    step([](int v) { return dpp_i<0x4E>(v); });    // quad_perm [2,3,0,1]
+    step([](int v) { return dpp_i<0x124>(v); });   // row_ror:4
+    step([](int v) { return dpp_i<0x128>(v); });   // row_ror:8
+    if constexpr (GROUP == 256) step([](int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); });
+    return d;
+}
+
+template <int BITS, int GROUP>
+__device__ __forceinline__ double clamp_cost(const float* t, const float* r, float z)
+{
+    constexpr float kQm = (float)((1 << BITS) - 1);
+    double d = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float c = __builtin_amdgcn_fmed3f(r[i], -z, kQm - z);
+        if (c != r[i]) {
+            const double cr = (double)c + (double)r[i];
+            d += ((double)c - (double)r[i]) * (cr - 2.0 * (double)t[i]);
+        }
+    }
+    return group_sum_f64<GROUP>(d);
+}
+
+template <int BITS, int GROUP>
+__device__ __forceinline__ float search_zero(const float* u, float inv, float z0)
+{
+    constexpr float kQm = (float)((1 << BITS) - 1);
+    float t[8], r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        t[i] = u[i] * inv;
+        r[i] = __builtin_rintf(t[i]);
+    }
+    float z = z0;
+    double dz = clamp_cost<BITS, GROUP>(t, r, z);
+    bool down = false;
+    if (z > 0.0f) {
+        const double dm = clamp_cost<BITS, GROUP>(t, r, z - 1.0f);
+        if (dm <= dz) { z -= 1.0f; dz = dm; down = true; }
+    }
+    if (down) {
+        while (z > 0.0f) {
+            const double dm = clamp_cost<BITS, GROUP>(t, r, z - 1.0f);
+            if (!(dm <= dz)) break;
+            z -= 1.0f; dz = dm;
+        }
+    } else {
+        while (z < kQm) {
+            const double dp = clamp_cost<BITS, GROUP>(t, r, z + 1.0f);
+            if (!(dp < dz)) break;
+            z += 1.0f; dz = dp;
+        }
+    }
+    return z;
+}
+
 // Quantize the lane's 8 values of one group (the whole group cooperates),
 // store codes and parameters, and return the codes (as integer-valued floats)
 // in q and the group's parameters.  `lane` is the lane within the wavefront.
@@ -384,7 +465,13 @@ __device__ __forceinline__ QParams quantize_group(const float* u, bool active, u
     float lo, hi;
     lane_stats<QUANT>(u, lo, hi);
     group_minmax<GROUP>(lo, hi);
-    const QParams p = make_params<BITS, QUANT>(lo, hi);
+    QParams p = make_params<BITS, QUANT>(lo, hi);
+    if constexpr (QUANT == kMse) {
+        if (p.s != 0.0f) {          // an all-zero group keeps z = 0
+            p.zf = search_zero<BITS, GROUP>(u, p.inv, p.zf);
+            p.word = (p.word & 0xFFFFu) | (f32_to_f16_bits(p.zf) << 16);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = quant1<BITS, QUANT>(u[i], p);
     if (active) {
@@ -650,7 +737,7 @@ struct ReduceArgs {
 // whenever an fp32 stream is staged), which also sets how many blocks share a
 // CU.
 template <int BITS, int U, bool UPD, int QUANT, int GROUP>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 4 && !UPD ? 6 : 1))) void reduce_kernel(const ReduceArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 4 && !UPD && QUANT != kMse ? 6 : 1))) void reduce_kernel(const ReduceArgs a)
 {
     using Io = Fp32Io<U, UPD>;
     extern __shared__ float lds[];

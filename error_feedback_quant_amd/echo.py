@@ -32,7 +32,8 @@ OUT_F32, OUT_BF16 = 0, 1
 ERR_NEGATED = 1
 QUANT_NAIVE, QUANT_SYMMETRIC = 2, 4
 X_ALL = 8
-QUANTS = {"zero_aware": 0, "naive": QUANT_NAIVE, "symmetric": QUANT_SYMMETRIC}
+QUANT_MSE = 16
+QUANTS = {"zero_aware": 0, "naive": QUANT_NAIVE, "symmetric": QUANT_SYMMETRIC, "mse": QUANT_MSE}
 MAX_P = 8
 
 

@@ -78,7 +78,8 @@ enum {
     ECHO_ERR_NEGATED = 1,      /* write -e (the next call's compensation) instead of e */
     ECHO_QUANT_NAIVE = 2,      /* Table 8 ablation: naive zero point */
     ECHO_QUANT_SYMMETRIC = 4,  /* Table 8 ablation: symmetric grid */
-    ECHO_X_ALL = 8             /* echo_gemm_quantize_ef only: write x for every segment */
+    ECHO_X_ALL = 8,            /* echo_gemm_quantize_ef only: write x for every segment */
+    ECHO_QUANT_MSE = 16        /* full method with its zero point searched for the least squared error */
 };
 
 #define ECHO_MAX_P 8
@@ -121,7 +122,12 @@ typedef struct echo_qparam {
  *                         with the clamps above; z = 2^(bits-1);
  *                         q = clamp(rint(u * (1/s)) + z, 0, Qm); a == 0 gives
  *                         s = +0 and all codes z.
- * Setting both is ECHO_EINVAL.
+ * ECHO_QUANT_MSE keeps the full method's s and codes rule and searches the
+ * integer zero point instead of taking the closed form: the z in [0, Qm]
+ * minimizing sum_i (clamp(rint(t_i) + z, 0, Qm) - z - t_i)^2 with
+ * t_i = u_i * (1/s), the smallest z on ties (it differs from the closed form
+ * only where the rounded codes span more than 2^bits levels).
+ * Setting more than one quantizer bit is ECHO_EINVAL.
  *
  *   x_bf16 (device, in)   bfloat16 bits [n] of this rank's partial sums
  *   comp   (device, in)   fp32 [n] compensation, or NULL (no feedback)
@@ -278,7 +284,7 @@ typedef struct echo_sim_args {
     int tiles;      /* tiles per segment, >= 1 (capped at S/group and at 4096) */
     int out_dtype;  /* ECHO_OUT_F32 or ECHO_OUT_BF16 */
     int ef;         /* 0: no compensation; 1: compensation on */
-    int quant;      /* 0 (zero-aware), ECHO_QUANT_NAIVE or ECHO_QUANT_SYMMETRIC */
+    int quant;      /* 0 (zero-aware), ECHO_QUANT_NAIVE, ECHO_QUANT_SYMMETRIC or ECHO_QUANT_MSE */
     float alpha;    /* fast fraction, 0 < alpha <= 1 */
     float beta;     /* slow release rate, 0 <= beta <= 1 */
     int64_t n;      /* elements per rank */

@@ -91,6 +91,8 @@ INT_CASES = [
     (256, 256, 256, 1, 4, "zero_aware", "err", 128),
     (512, 512, 128, 4, 4, "zero_aware", "negated_in_place", 256),
     (512, 256, 192, 2, 8, "naive", "err", 256),
+    (512, 512, 128, 4, 4, "mse", "negated_in_place", 128),
+    (512, 256, 192, 2, 8, "mse", "err", 256),
 ]
 
 

@@ -269,11 +269,12 @@ def variant_inputs(P, n, seed):
 
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("group", [128, 256])
-@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric"])
+@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric", "mse"])
 def test_quantizer_variants_each_step(echo, quant, group, bits):
-    """Table 8's quantizers (full method, naive zero point, symmetric grid) and
-    its group size 256: push, owner reduce and tail decode, step by step, bit
-    for bit against the oracle, on whole segments and a ragged tile."""
+    """Table 8's quantizers (full method, naive zero point, symmetric grid),
+    the full method with its zero point searched, and group size 256: push,
+    owner reduce and tail decode, step by step, bit for bit against the
+    oracle, on whole segments and a ragged tile."""
     P = 4
     n = P * 256 * 19                      # 19 groups of 256 (38 rows) per segment
     Sn = n // P
@@ -327,7 +328,7 @@ def test_quantizer_variants_each_step(echo, quant, group, bits):
             assert_bits_equal(got, want, "decoded output")
 
 
-@pytest.mark.parametrize("quant", ["naive", "symmetric"])
+@pytest.mark.parametrize("quant", ["naive", "symmetric", "mse"])
 def test_quantizer_variant_edge_groups(echo, quant):
     """The edge groups of the full method's test, through each ablation."""
     flag = echo.QUANTS[quant]
@@ -348,3 +349,60 @@ def test_quantizer_variant_edge_groups(echo, quant):
             assert_bits_equal(host_u8(cd), wc, "edge codes")
             assert_bits_equal(host_u16(pd), wp, "edge params")
             assert_bits_equal(host_f32(ed), we, "edge err")
+
+
+def search_groups(bits, group, count, seed):
+    """Groups whose searched zero point differs from the closed form (chosen
+    by the oracle), mixed with groups where it does not: one-decimal values
+    (the shape of Fig. 4's example) and Laplace draws."""
+    rng = np.random.default_rng(seed)
+    moved, kept = [], []
+    while len(moved) < count // 2 or len(kept) < count - count // 2:
+        if rng.random() < 0.5:
+            v = (rng.integers(-40, 41, size=group) / 10).astype(np.float32)
+            v[rng.integers(0, group, size=group - 4)] = 0.0     # few nonzeros: the span decides
+        else:
+            v = (rng.laplace(size=group) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32)
+        _, _, zh = oracle.quantize_group(v, bits, "mse")
+        _, _, zh0 = oracle.quantize_group(v, bits)
+        (moved if zh != zh0 else kept).append(v)
+    return moved[:count // 2] + kept[:count - count // 2]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [128, 256])
+def test_zero_point_search_moves_the_zero_point(echo, bits, group):
+    """The searched zero point through push and owner reduce, on groups where
+    it differs from the closed form (half of them) and where it does not,
+    bit for bit against the oracle."""
+    P, count = 4, 32
+    groups = search_groups(bits, group, count, 300 + bits + group)
+    n = group * count
+    Sn = n // P
+    comp = np.concatenate(groups).astype(np.float32)
+    x = np.zeros(n, np.uint16)
+    cb = oracle.code_bytes(n, bits)
+    flag = echo.QUANT_MSE
+    pc_h, pp_h, pc_d, pp_d = [], [], [], []
+    for rank in range(P):
+        say("zero-point search push", bits, group, rank)
+        wc = np.zeros(cb, np.uint8); wp = np.zeros(2 * n // group, np.uint16); we = np.zeros(n, np.float32)
+        oracle.quantize_ef(x, comp, n, P, rank, 0, Sn, bits, group, wc, wp, we, flag)
+        cd = dev_u8(np.zeros(cb, np.uint8)); pd = params_dev(n // group, 0); ed = dev_f32(np.zeros(n, np.float32))
+        echo.echo_quantize_ef(dev_u16(x), dev_f32(comp), n, P, rank, 0, Sn, bits, group, cd, pd, ed, flag)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u8(cd), wc, "search codes")
+        assert_bits_equal(host_u16(pd), wp, "search params")
+        assert_bits_equal(host_f32(ed), we, "search err")
+        pc_h.append(wc); pp_h.append(wp); pc_d.append(cd); pp_d.append(pd)
+    # the owner's sum of the same groups, requantized with the search
+    say("zero-point search reduce", bits, group)
+    sc_h = np.zeros(cb, np.uint8); sp_h = np.zeros(2 * n // group, np.uint16)
+    sc_d, sp_d = dev_u8(sc_h), dev_u16(sp_h)
+    for o in range(P):
+        oracle.reduce_segment(x, comp, pc_h, pp_h, P, o, n, 0, Sn, bits, group, sc_h, sp_h, None, flag)
+        echo.echo_reduce_segment(dev_u16(x), dev_f32(comp), pc_d, pp_d, P, o, n, 0, Sn, bits, group, sc_d,
+                                 sp_d, None, flag)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u8(sc_d), sc_h, "search sum codes")
+    assert_bits_equal(host_u16(sp_d), sp_h, "search sum params")

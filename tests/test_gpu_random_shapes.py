@@ -44,7 +44,7 @@ def draw(i):
     g0 = int(rng.integers(0, groups))
     gl = int(rng.integers(1, groups - g0 + 1))
     return dict(P=P, G=G, S=groups * G, tb=g0 * G, tl=gl * G, bits=int(rng.choice([4, 8])),
-                quant=str(rng.choice(["zero_aware", "naive", "symmetric"])),
+                quant=str(rng.choice(["zero_aware", "naive", "symmetric", "mse"])),
                 ef=str(rng.choice(["off", "err", "negated"])),
                 odt=int(rng.choice([oracle.OUT_F32, oracle.OUT_BF16])),
                 dist=str(rng.choice(["normal", "laplace", "one_sided", "sparse"])), seed=9100 + i)

@@ -120,6 +120,8 @@ VARIANT_CASES = [
     (8, 8, "classic_unfused", oracle.OUT_F32, 3, 2, "naive", 256),
     (3, 4, "two", oracle.OUT_F32, 2, 3, "symmetric", 256),
     (2, 8, "off", oracle.OUT_BF16, 1, 1, "naive", 128),
+    (4, 4, "classic", oracle.OUT_BF16, 3, 2, "mse", 128),
+    (5, 8, "two_fused", oracle.OUT_F32, 2, 3, "mse", 256),
 ]
 
 

@@ -174,20 +174,21 @@ def test_onegb_full_parity(echo, P):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("mode", ["ef_off", "f32_out", "two_timescale", "bits8", "naive", "symmetric", "g256"])
+@pytest.mark.parametrize("mode", ["ef_off", "f32_out", "two_timescale", "bits8", "naive", "symmetric", "g256",
+                                  "mse"])
 def test_onegb_full_parity_modes(echo, mode):
     """The benchmark's other legs at full size (1 GiB message, P = 4, one tile
     on one stream): feedback off, fp32 output, the two-timescale compensator
     (alpha = 0.5, beta = 0.25) fused into push and reduce, 8-bit codes, and
-    Table 8's naive-zero-point and symmetric-grid quantizers and groups of
-    256.  Two calls carry the state; every output, compensation and
+    Table 8's naive-zero-point and symmetric-grid quantizers, groups of
+    256, and the full method with its zero point searched.  Two calls carry the state; every output, compensation and
     slow-memory element matches the oracle's whole call bit for bit."""
     P, n = 4, 1 << 29
     L = 1 << 18
     ef = mode != "ef_off"
     two = mode == "two_timescale"
     bits = 8 if mode == "bits8" else 4
-    quant = mode if mode in ("naive", "symmetric") else "zero_aware"
+    quant = mode if mode in ("naive", "symmetric", "mse") else "zero_aware"
     group = 256 if mode == "g256" else 128
     odt = oracle.OUT_F32 if mode == "f32_out" else oracle.OUT_BF16
     alpha, beta = (0.5, 0.25) if two else (1.0, 0.0)
