@@ -1,4 +1,4 @@
-"""Seeded synthetic partial sums for the five workloads.
+"""Seeded synthetic partial sums for the five workloads and two study inputs.
 
 This module only draws random inputs; it holds none of the method's
 arithmetic, and both the GPU path's tests and the CPU oracle's tests take
@@ -31,9 +31,15 @@ a tensor-parallel block would produce):
             fp32 for any K below 2^24.
             Default shape: a Llama-3-8B MLP down projection at TP = 4 (4096
             tokens, hidden 4096, K = 14336 / 4 = 3584).
+  sparse    the chain workload's values with a Bernoulli(keep) mask of exact
+            zeros (keep = 0.5 by default): partial sums of sparse activations,
+            where most groups hold both signs and many exact zeros.
+  shifted   the chain workload's values plus a per-channel positive mean
+            0.15 * |N(0,1)| * sigma_h (drawn once), so that many groups are
+            one-sided, as after a gated or rectified activation.
 
 Seed of (workload, step, site, rank): 20261202 + 1000003*w + 10007*step +
-101*site + rank, with w = 1..6 in the order above.
+101*site + rank, with w = 1..8 in the order above.
 """
 from __future__ import annotations
 
@@ -41,7 +47,8 @@ import math
 
 import torch
 
-WORKLOADS = {"single": 1, "chain": 2, "onegb": 3, "chain8": 4, "training": 5, "tpblock": 6}
+WORKLOADS = {"single": 1, "chain": 2, "onegb": 3, "chain8": 4, "training": 5, "tpblock": 6, "sparse": 7,
+             "shifted": 8}
 
 SHAPES = {
     "single": dict(P=4, tokens=64, hidden=1024, bits=4, sites=1),
@@ -88,6 +95,23 @@ def chain(rank: int, site: int, tokens: int = 2048, hidden: int = 4096,
         sigma_h = chain_channel_scale(hidden, chain_seed, device=device)
     g = _gen(seed_of("chain", chain_seed, site, rank), device=device)
     x = 0.02 * torch.randn(tokens, hidden, generator=g, dtype=torch.float32, device=device) * sigma_h
+    return _bf16_bits(x.reshape(-1))
+
+
+def sparse(rank: int, site: int, tokens: int, hidden: int, sigma_h: torch.Tensor, keep: float = 0.5,
+           device="cpu") -> torch.Tensor:
+    g = _gen(seed_of("sparse", 0, site, rank), device=device)
+    x = 0.02 * torch.randn(tokens, hidden, generator=g, dtype=torch.float32, device=device) * sigma_h
+    mask = torch.rand(tokens, hidden, generator=g, device=device) < keep
+    x = torch.where(mask, x, torch.zeros((), device=device))
+    return _bf16_bits(x.reshape(-1))
+
+
+def shifted(rank: int, site: int, tokens: int, hidden: int, sigma_h: torch.Tensor, device="cpu") -> torch.Tensor:
+    gm = _gen(seed_of("shifted", 0, 0, 0) + 7, device=device)
+    mu = 0.15 * torch.randn(hidden, generator=gm, dtype=torch.float32, device=device).abs() * sigma_h
+    g = _gen(seed_of("shifted", 0, site, rank), device=device)
+    x = 0.02 * torch.randn(tokens, hidden, generator=g, dtype=torch.float32, device=device) * sigma_h + mu
     return _bf16_bits(x.reshape(-1))
 
 

@@ -13,9 +13,18 @@ qualitative facts that do not depend on a model:
     rows agree to 0.1 %);
   * feedback keeps the accumulated error bounded for every quantizer.
 On these Gaussian partial sums the naive zero point falls between the full
-method and the symmetric grid, while Table 8 ranks it last; real activations
-(outlier channels, one-sided groups) are outside what the synthetic data
-models.
+method and the symmetric grid, while Table 8 ranks it last.  Two more
+synthetic inputs (4 bits, no feedback, per-call error) show where each
+ablation loses:
+  * partial sums of sparse activations (half the elements exact zeros, both
+    signs in most groups): the naive zero point puts 0 off the grid, so every
+    zero carries an error, and it falls last -- Table 8's 4-bit ordering,
+    full method < symmetric grid < naive zero point;
+  * groups shifted to one side by a per-channel positive mean: the symmetric
+    grid spends half its codes on values that never occur and falls last.
+The full method with its zero point searched for the least squared error
+stays within 1 % of the closed form everywhere: with the scale fixed by the
+range, the search can only trade clamping at the two ends of the range.
 """
 import numpy as np
 import pytest
@@ -25,6 +34,7 @@ from error_feedback_quant_amd import inputs
 
 P, TOKENS, HIDDEN, N = 4, 16, 1024, 32
 QUANTS = ("zero_aware", "naive", "symmetric")
+N_SHAPED = 8              # sites of the sparse and shifted inputs
 
 
 def rms(a):
@@ -53,6 +63,21 @@ def study():
                     delta=np.mean([rms(d) for d in off["delta"]]) / signal,
                     ef_max=max(rms(e) for e in ef["E"]) / signal,
                     off_end=rms(off["E"][-1]) / signal)
+    # the sparse and shifted inputs: per-call error at 4 bits, every quantizer
+    for kind in ("sparse", "shifted"):
+        gen = getattr(inputs, kind)
+
+        def shaped(site, gen=gen):
+            if site >= N_SHAPED:
+                return None
+            return [inputs.as_numpy_u16(gen(r, site, TOKENS, HIDDEN, sigma)) for r in range(P)]
+
+        xs0 = shaped(0)
+        sig = rms(sum((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64) for x in xs0))
+        for g in (128, 256):
+            for q in QUANTS + ("mse",):
+                off = oracle.depth_chain(shaped, P, n, bits=4, group=g, ef=False, quant=q)
+                res[(kind, g, q)] = dict(delta=np.mean([rms(d) for d in off["delta"]]) / sig)
     return res
 
 
@@ -77,7 +102,29 @@ def test_eight_bit_zero_aware_and_naive_nearly_tie(study):
         assert study[(8, g, "zero_aware")]["delta"] < 0.1 * study[(4, g, "zero_aware")]["delta"]
 
 
+def test_sparse_partials_rank_the_naive_zero_point_last(study):
+    """Table 8's 4-bit ordering: full method < symmetric grid < naive zero point."""
+    for g in (128, 256):
+        za, sym, nv = (study[("sparse", g, q)]["delta"] for q in QUANTS[:1] + ("symmetric", "naive"))
+        assert za < sym < nv, (g, za, sym, nv)
+
+
+def test_shifted_groups_rank_the_symmetric_grid_last(study):
+    for g in (128, 256):
+        za, nv, sym = (study[("shifted", g, q)]["delta"] for q in QUANTS)
+        assert za < nv < sym, (g, za, nv, sym)
+
+
+def test_searched_zero_point_stays_with_the_closed_form(study):
+    for kind in ("sparse", "shifted"):
+        for g in (128, 256):
+            za, ms = study[(kind, g, "zero_aware")]["delta"], study[(kind, g, "mse")]["delta"]
+            assert abs(ms - za) <= 0.01 * za, (kind, g, za, ms)
+
+
 def test_feedback_bounds_the_error_for_every_quantizer(study):
     for key, v in study.items():
+        if "ef_max" not in v:
+            continue
         assert v["ef_max"] <= 1.5 * v["delta"], key
         assert v["off_end"] >= 3.0 * v["ef_max"], key
