@@ -137,7 +137,10 @@ struct ReduceL {
         const bool comp = a.comp[0] != nullptr, err = a.err[0] != nullptr;
         size_t lds = (UP || comp || err) ? Io::kLdsFloats * sizeof(float) : 0;
         if ((UP || comp) && lds < kReduceCompLds) lds = kReduceCompLds;
-        hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G>), grid, dim3(echo::kBlock), lds, st, a);
+        if (a.P <= 4)
+            hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G, 4>), grid, dim3(echo::kBlock), lds, st, a);
+        else
+            hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G, 8>), grid, dim3(echo::kBlock), lds, st, a);
     }
 };
 

@@ -70,6 +70,14 @@ __device__ __forceinline__ void st_stream(T* p, const T& v)
     __builtin_nontemporal_store(v, p);
 }
 
+// A buffer resource over `base` (raw bytes, no range limit in practice):
+// loads through it take a wave-uniform base from SGPRs and a 32-bit lane
+// offset.  aux = 2 sets the non-temporal bit, as the streams above.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
 // fp32 streams (compensation in, error out) go through a wave-private LDS
 // slice so that every global fp32 access is lane-contiguous (1 KB per wave
 // instruction) while the arithmetic keeps 8 consecutive elements per lane.
@@ -294,13 +302,21 @@ struct Packed<4> {
         }
         w = ev | (od << 4);
     }
-    __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
+    // e0: element offset from `codes`' element 0 (a 32-bit lane offset from a
+    // block's base, or a 64-bit message offset)
+    template <typename Off>
+    __device__ __forceinline__ void store(uint8_t* codes, Off e0) const
     {
         st_stream((uint32_t*)(codes + (e0 >> 1)), w);
     }
-    __device__ __forceinline__ void load(const uint8_t* codes, int64_t e0)
+    template <typename Off>
+    __device__ __forceinline__ void load(const uint8_t* codes, Off e0)
     {
         w = ld_stream((const uint32_t*)(codes + (e0 >> 1)));
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t codes, uint32_t e0)
+    {
+        w = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(codes, (int)(e0 >> 1), 0, 2);
     }
     __device__ __forceinline__ void unpack(float* q) const
     {
@@ -329,13 +345,19 @@ struct Packed<8> {
         w.x = x;
         w.y = y;
     }
-    __device__ __forceinline__ void store(uint8_t* codes, int64_t e0) const
+    template <typename Off>
+    __device__ __forceinline__ void store(uint8_t* codes, Off e0) const
     {
         st_stream((u32x2*)(codes + e0), w);
     }
-    __device__ __forceinline__ void load(const uint8_t* codes, int64_t e0)
+    template <typename Off>
+    __device__ __forceinline__ void load(const uint8_t* codes, Off e0)
     {
         w = ld_stream((const u32x2*)(codes + e0));
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t codes, uint32_t e0)
+    {
+        w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(codes, (int)e0, 0, 2));
     }
     __device__ __forceinline__ void unpack(float* q) const
     {
@@ -458,8 +480,10 @@ __device__ __forceinline__ float search_zero(const float* u, float inv, float z0
 // Quantize the lane's 8 values of one group (the whole group cooperates),
 // store codes and parameters, and return the codes (as integer-valued floats)
 // in q and the group's parameters.  `lane` is the lane within the wavefront.
-template <int BITS, int QUANT, int GROUP>
-__device__ __forceinline__ QParams quantize_group(const float* u, bool active, uint32_t lane, int64_t e0,
+// codes, params and e0 as for Packed: e0 counts elements from the element
+// that codes[0] and params[0] describe.
+template <int BITS, int QUANT, int GROUP, typename Off>
+__device__ __forceinline__ QParams quantize_group(const float* u, bool active, uint32_t lane, Off e0,
                                                   uint8_t* codes, uint32_t* params, float* q)
 {
     float lo, hi;
@@ -494,20 +518,38 @@ __device__ __forceinline__ void group_error(const float* q, const QParams& p, co
     }
 }
 
+// Addressing: a block works on rows [rb, rb + 16 U) of its tile (rows of 128
+// elements).  Its loads and stores go through wave-uniform base pointers at
+// the block's first element plus a 32-bit lane offset (a block spans at most
+// 16 U * 128 elements), so the per-lane address needs no 64-bit arithmetic.
+//
 // Where the lane-contiguous fp32 accesses of a wave land: half h (0/1) of the
 // wave's 512-element chunk covers rows 2h and 2h+1; lane l moves the float4 at
 // offset (4 l) mod 128 of row 2h + l/32.  Rows past the tile re-read the last
 // row (clamped) and are never stored.
+// Row of a block, from the block's row 0.  A block spans 16 U rows (U a
+// power of two) and every row it touches lies in [rb, rb + 16 U), so the
+// mask changes nothing; it shows the compiler that the lane offsets stay
+// small, which lets every access use a scalar base and a 32-bit lane offset.
+template <int U>
+__device__ __forceinline__ uint32_t block_row(uint32_t row, uint32_t rb)
+{
+    static_assert((U & (U - 1)) == 0, "passes per block must be a power of two");
+    return (row - rb) & (uint32_t)(kRowsPerBlock * U - 1);
+}
+
 struct WaveMap {
-    int64_t seg0;          // first element of the tile in this segment
+    uint32_t rb;           // row index (within the tile) of the block's row 0
     uint32_t gw;           // row index (within the tile) of the wave's row 0
     uint32_t last;         // tile_rows - 1
     uint32_t lane;
+    uint32_t mask;         // rows per block - 1 (a power of two minus one)
     __device__ __forceinline__ uint32_t row(uint32_t r) const { return gw + r; }
-    __device__ __forceinline__ int64_t contig(uint32_t h) const
+    // element offset from the block's first element of this lane's float4 of half h
+    __device__ __forceinline__ uint32_t contig(uint32_t h) const
     {
         const uint32_t g = min(gw + 2u * h + (lane >> 5), last);
-        return seg0 + (int64_t)g * kRow + (int64_t)((4u * lane) & (kRow - 1));
+        return ((g - rb) & mask) * kRow + ((4u * lane) & (kRow - 1));
     }
     __device__ __forceinline__ bool contig_active(uint32_t h) const { return gw + 2u * h + (lane >> 5) <= last; }
 };
@@ -534,7 +576,8 @@ __device__ __forceinline__ void natural_write(float* slice, uint32_t lane, const
 // ------------------------------------------- fp32 stream I/O of a wavefront --
 // Loads the compensation (and, for UPD, the slow memory) of U passes, and
 // writes back either the error (err) or the updated compensation and slow
-// memory, lane-contiguously through the wave's LDS slices when staging.
+// memory, lane-contiguously through the wave's LDS slices.  The pointers are
+// the block's bases (its first element).
 
 template <int U, bool UPD>
 struct Fp32Io {
@@ -591,7 +634,7 @@ struct Fp32Io {
 #pragma unroll
             for (uint32_t h = 0; h < 2; ++h) {
                 if (!wm[k].contig_active(h)) continue;
-                const int64_t g = wm[k].contig(h);
+                const uint32_t g = wm[k].contig(h);
                 st_stream((f32x4*)(dst0 + g), *(const f32x4*)(slice(lds, k, 0, wave) + 256 * h + 4 * lane));
                 if (UPD) st_stream((f32x4*)(dst1 + g), *(const f32x4*)(slice(lds, k, 1, wave) + 256 * h + 4 * lane));
             }
@@ -654,12 +697,15 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
     const uint32_t seg = si + (si >= rank ? 1u : 0u);
     const int64_t seg0 = (int64_t)seg * a.S + a.tile_begin;
     const uint32_t last = a.tile_rows - 1u;
-    const uint16_t* const x = a.x[z];
-    float* const comp = (float*)a.comp[z];
-    float* const slow = a.slow[z];
-    float* const err = a.err[z];
-    uint8_t* const codes = a.codes[z];
-    uint32_t* const params = a.params[z];
+    // block bases (the block's first element) and 32-bit lane offsets from them
+    const uint32_t rb = blockIdx.x * (uint32_t)(kRowsPerBlock * U);
+    const int64_t blk0 = seg0 + (int64_t)rb * kRow;
+    const uint16_t* const x = a.x[z] + blk0;
+    float* const comp = a.comp[z] ? (float*)a.comp[z] + blk0 : nullptr;
+    float* const slow = UPD ? a.slow[z] + blk0 : nullptr;
+    float* const err = a.err[z] ? a.err[z] + blk0 : nullptr;
+    uint8_t* const codes = a.codes[z] + blk0 * BITS / 8;
+    uint32_t* const params = a.params[z] + blk0 / GROUP;
     const bool has_comp = UPD || comp != nullptr;
     const bool has_out = UPD || err != nullptr;
 
@@ -668,12 +714,13 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
     Io io;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        wm[k].seg0 = seg0;
-        wm[k].gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
+        wm[k].rb = rb;
+        wm[k].mask = (uint32_t)(kRowsPerBlock * U - 1);
+        wm[k].gw = rb + (uint32_t)k * kRowsPerBlock + 4u * wave;
         wm[k].last = last;
         wm[k].lane = lane;
-        const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
-        xv[k] = ld_stream((const u32x4*)(x + e0));
+        const uint32_t o = block_row<U>(min(wm[k].row(rw), last), rb) * kRow + l16 * kEPL;
+        xv[k] = ld_stream((const u32x4*)(x + o));
         if (has_comp) io.load(k, wm[k], comp, slow);
     }
     if (has_comp) io.stage(lds, wave, lane);
@@ -681,7 +728,7 @@ __global__ __launch_bounds__(kBlock) void push_kernel(const PushArgs a)
     for (int k = 0; k < U; ++k) {
         const uint32_t graw = wm[k].row(rw);
         const bool active = graw <= last;
-        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kRow + (int64_t)(l16 * kEPL);
+        const uint32_t e0 = block_row<U>(min(graw, last), rb) * kRow + l16 * kEPL;
         float u[8];
         unpack_bf16x8(xv[k], u);
         if (has_comp) {
@@ -731,12 +778,14 @@ struct ReduceArgs {
 };
 
 // grid: (ceil(tile_rows / (16 U)), owners).  UPD as for push_kernel.  The
-// peer loop is unrolled to kMaxP with uniform guards on the runtime P.
+// peer loop is unrolled to MAXP (4 or 8, at least P) with uniform guards on
+// the runtime P: the registers that hold the peers' codes in flight are
+// sized for MAXP ranks, so a launch with P <= 4 takes the 4-rank instance.
 //
 // LDS is dynamic: the launcher sizes it (at least Io::kLdsFloats floats
 // whenever an fp32 stream is staged), which also sets how many blocks share a
 // CU.
-template <int BITS, int U, bool UPD, int QUANT, int GROUP>
+template <int BITS, int U, bool UPD, int QUANT, int GROUP, int MAXP>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 4 && !UPD && QUANT != kMse ? 6 : 1))) void reduce_kernel(const ReduceArgs a)
 {
     using Io = Fp32Io<U, UPD>;
@@ -749,32 +798,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
     const int owner = a.owner0 + (int)y;
     const int64_t seg0 = (int64_t)owner * a.S + a.tile_begin;
     const uint32_t last = a.tile_rows - 1u;
-    const uint16_t* const x = a.x[y];
-    float* const comp = (float*)a.comp[y];
-    float* const slow = a.slow[y];
-    float* const err = a.err[y];
+    // block bases (the block's first element) and 32-bit lane offsets from them
+    const uint32_t rb = blockIdx.x * (uint32_t)(kRowsPerBlock * U);
+    const int64_t blk0 = seg0 + (int64_t)rb * kRow;
+    const uint16_t* const x = a.x[y] + blk0;
+    float* const comp = a.comp[y] ? (float*)a.comp[y] + blk0 : nullptr;
+    float* const slow = UPD ? a.slow[y] + blk0 : nullptr;
+    float* const err = a.err[y] ? a.err[y] + blk0 : nullptr;
     const bool has_comp = UPD || comp != nullptr;
     const bool has_out = UPD || err != nullptr;
 
     WaveMap wm[U];
     u32x4 xv[U];
     Io io;
-    Packed<BITS> pk[U][kMaxP];
-    uint32_t pw[U][kMaxP];
+    Packed<BITS> pk[U][MAXP];
+    uint32_t pw[U][MAXP];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        wm[k].seg0 = seg0;
-        wm[k].gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
+        wm[k].rb = rb;
+        wm[k].mask = (uint32_t)(kRowsPerBlock * U - 1);
+        wm[k].gw = rb + (uint32_t)k * kRowsPerBlock + 4u * wave;
         wm[k].last = last;
         wm[k].lane = lane;
-        const int64_t e0 = seg0 + (int64_t)min(wm[k].row(rw), last) * kRow + (int64_t)(l16 * kEPL);
-        xv[k] = ld_stream((const u32x4*)(x + e0));
+        const uint32_t o = block_row<U>(min(wm[k].row(rw), last), rb) * kRow + l16 * kEPL;
+        xv[k] = ld_stream((const u32x4*)(x + o));
         if (has_comp) io.load(k, wm[k], comp, slow);
 #pragma unroll
-        for (int j = 0; j < kMaxP; ++j) {
+        for (int j = 0; j < MAXP; ++j) {
             if (j < a.P && j != owner) {
-                pk[k][j].load(a.pc[j], e0);
-                pw[k][j] = a.pp[j][e0 / GROUP];
+                pk[k][j].load(stream_rsrc(a.pc[j] + blk0 * BITS / 8), o);
+                pw[k][j] = (a.pp[j] + blk0 / GROUP)[o / GROUP];
             }
         }
     }
@@ -783,7 +836,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
     for (int k = 0; k < U; ++k) {
         const uint32_t graw = wm[k].row(rw);
         const bool active = graw <= last;
-        const int64_t e0 = seg0 + (int64_t)min(graw, last) * kRow + (int64_t)(l16 * kEPL);
+        const uint32_t e0 = block_row<U>(min(graw, last), rb) * kRow + l16 * kEPL;
         float own[8];
         unpack_bf16x8(xv[k], own);
         if (has_comp) {
@@ -795,7 +848,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
         // fp32 sum in rank order; the owner's own term enters unquantized
         float acc[8];
 #pragma unroll
-        for (int j = 0; j < kMaxP; ++j) {
+        for (int j = 0; j < MAXP; ++j) {
             if (j >= a.P) break;
             if (j == owner) {
 #pragma unroll
@@ -809,7 +862,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
             }
         }
         float q[8], e[8];
-        const QParams p = quantize_group<BITS, QUANT, GROUP>(acc, active, lane, e0, a.sc, a.sp, q);
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(acc, active, lane, e0, a.sc + blk0 * BITS / 8,
+                                                             a.sp + blk0 / GROUP, q);
         if (UPD) {
             group_error(q, p, acc, false, e);
             float m[8], cn[8], mn[8];
@@ -852,23 +906,28 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
     const uint32_t l16 = threadIdx.x & 15u;
     const uint32_t row = threadIdx.x >> 4;
     const int64_t seg0 = (int64_t)blockIdx.y * a.S + a.tile_begin;
-    const uint32_t g0 = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + row;
-    void* const out = a.out[blockIdx.z];
+    // block bases (the block's first element) and 32-bit lane offsets from them
+    const uint32_t rb = blockIdx.x * (uint32_t)(kRowsPerBlock * U);
+    const int64_t blk0 = seg0 + (int64_t)rb * kRow;
+    const uint32_t g0 = rb + row;
+    const uint8_t* const sc = a.sc + blk0 * BITS / 8;
+    const uint32_t* const sp = a.sp + blk0 / GROUP;
+    void* const out = OUT_BF16 ? (void*)((uint16_t*)a.out[blockIdx.z] + blk0) : (void*)((float*)a.out[blockIdx.z] + blk0);
 
     Packed<BITS> pk[U];
     uint32_t pw[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const uint32_t gi = min(g0 + (uint32_t)(k * kRowsPerBlock), a.tile_rows - 1u);
-        const int64_t e0 = seg0 + (int64_t)gi * kRow + (int64_t)(l16 * kEPL);
-        pk[k].load(a.sc, e0);
-        pw[k] = a.sp[e0 / GROUP];
+        const uint32_t o = block_row<U>(gi, rb) * kRow + l16 * kEPL;
+        pk[k].load(sc, o);
+        pw[k] = sp[o / GROUP];
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const uint32_t graw = g0 + (uint32_t)(k * kRowsPerBlock);
         if (graw >= a.tile_rows) continue;
-        const int64_t e0 = seg0 + (int64_t)graw * kRow + (int64_t)(l16 * kEPL);
+        const uint32_t o = block_row<U>(graw, rb) * kRow + l16 * kEPL;
         float q[8], v[8];
         pk[k].unpack(q);
         decode8(q, pw[k], v);
@@ -878,7 +937,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
             w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
             w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
             w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
-            st_stream((u32x4*)((uint16_t*)out + e0), w);
+            st_stream((u32x4*)((uint16_t*)out + o), w);
         } else {
             natural_write(lds + (k * (kBlock / 64) + wave) * kWaveChunk, lane, v);
         }
@@ -889,8 +948,9 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a)
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             WaveMap wm;
-            wm.seg0 = seg0;
-            wm.gw = blockIdx.x * (uint32_t)(kRowsPerBlock * U) + (uint32_t)k * kRowsPerBlock + 4u * wave;
+            wm.rb = rb;
+            wm.mask = (uint32_t)(kRowsPerBlock * U - 1);
+            wm.gw = rb + (uint32_t)k * kRowsPerBlock + 4u * wave;
             wm.last = a.tile_rows - 1u;
             wm.lane = lane;
             const float* sl = lds + (k * (kBlock / 64) + wave) * kWaveChunk;
