@@ -66,6 +66,7 @@ def test_quantize_ef_argument_checks():
     assert q(x=None) == echo.EINVAL and q(codes=None) == echo.EINVAL
     assert q(x=FAKE + 8) == echo.EALIGN and q(comp=FAKE + 4) == echo.EALIGN
     assert q(flags=8) == echo.EINVAL and q(flags=6) == echo.EINVAL   # unknown bit; both ablations
+    assert q(flags=18) == echo.EINVAL and q(flags=20) == echo.EINVAL and q(flags=32) == echo.EINVAL
     assert q(n=1 << 35, P=4) == echo.ESHAPE             # beyond the 2^34 limit
     # empty work is a successful no-op (nothing to enqueue)
     assert q(tl=0) == 0 and q(n=0, tl=0) == 0 and q(P=1, tl=128) == 0
@@ -90,7 +91,7 @@ def test_gemm_quantize_ef_argument_checks():
     assert g(a=None) == echo.EINVAL and g(w=None) == echo.EINVAL and g(x_out=None) == echo.EINVAL
     assert g(codes=None) == echo.EINVAL
     assert g(a=FAKE + 2) == echo.EALIGN and g(err=FAKE + 4) == echo.EALIGN
-    assert g(flags=16) == echo.EINVAL and g(flags=6) == echo.EINVAL
+    assert g(flags=32) == echo.EINVAL and g(flags=6) == echo.EINVAL and g(flags=18) == echo.EINVAL
     assert g(M=0) == 0 and g(N=0) == 0                # nothing to compute
 
 
