@@ -137,10 +137,20 @@ struct ReduceL {
         const bool comp = a.comp[0] != nullptr, err = a.err[0] != nullptr;
         size_t lds = (UP || comp || err) ? Io::kLdsFloats * sizeof(float) : 0;
         if ((UP || comp) && lds < kReduceCompLds) lds = kReduceCompLds;
-        if (a.P <= 4)
-            hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G, 4>), grid, dim3(echo::kBlock), lds, st, a);
-        else
-            hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G, 8>), grid, dim3(echo::kBlock), lds, st, a);
+        // one owner at P = 4: the instance with that owner's sum order fixed
+        const int fixed = (a.P == 4 && grid.y == 1) ? a.owner0 : -1;
+#define ECHO_RED(MAXP, OWNER) \
+    hipLaunchKernelGGL((echo::reduce_kernel<B, kURed, UP, Q, G, MAXP, OWNER>), grid, dim3(echo::kBlock), lds, st, a)
+        switch (fixed) {
+        case 0: ECHO_RED(4, 0); break;
+        case 1: ECHO_RED(4, 1); break;
+        case 2: ECHO_RED(4, 2); break;
+        case 3: ECHO_RED(4, 3); break;
+        default:
+            if (a.P <= 4) ECHO_RED(4, -1);
+            else ECHO_RED(8, -1);
+        }
+#undef ECHO_RED
     }
 };
 

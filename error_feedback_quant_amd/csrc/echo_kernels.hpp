@@ -781,21 +781,26 @@ struct ReduceArgs {
 // peer loop is unrolled to MAXP (4 or 8, at least P) with uniform guards on
 // the runtime P: the registers that hold the peers' codes in flight are
 // sized for MAXP ranks, so a launch with P <= 4 takes the 4-rank instance.
+// OWNER >= 0 fixes P = MAXP and the owner (a one-owner launch) at compile
+// time: the rank-order sum is then straight-line code, without the register
+// moves that merge the owner's and the peers' branches.
 //
 // LDS is dynamic: the launcher sizes it (at least Io::kLdsFloats floats
 // whenever an fp32 stream is staged), which also sets how many blocks share a
 // CU.
-template <int BITS, int U, bool UPD, int QUANT, int GROUP, int MAXP>
+template <int BITS, int U, bool UPD, int QUANT, int GROUP, int MAXP, int OWNER>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 4 && !UPD && QUANT != kMse ? 6 : 1))) void reduce_kernel(const ReduceArgs a)
 {
+    constexpr bool kFixed = OWNER >= 0;
     using Io = Fp32Io<U, UPD>;
     extern __shared__ float lds[];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t l16 = lane & 15u;
     const uint32_t rw = lane >> 4;
-    const uint32_t y = blockIdx.y;
-    const int owner = a.owner0 + (int)y;
+    const uint32_t y = kFixed ? 0u : blockIdx.y;
+    const int owner = kFixed ? OWNER : a.owner0 + (int)y;
+    const int nranks = kFixed ? MAXP : a.P;
     const int64_t seg0 = (int64_t)owner * a.S + a.tile_begin;
     const uint32_t last = a.tile_rows - 1u;
     // block bases (the block's first element) and 32-bit lane offsets from them
@@ -825,7 +830,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
         if (has_comp) io.load(k, wm[k], comp, slow);
 #pragma unroll
         for (int j = 0; j < MAXP; ++j) {
-            if (j < a.P && j != owner) {
+            if (j < nranks && j != owner) {
                 pk[k][j].load(stream_rsrc(a.pc[j] + blk0 * BITS / 8), o);
                 pw[k][j] = (a.pp[j] + blk0 / GROUP)[o / GROUP];
             }
@@ -849,7 +854,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
         float acc[8];
 #pragma unroll
         for (int j = 0; j < MAXP; ++j) {
-            if (j >= a.P) break;
+            if (j >= nranks) break;
             if (j == owner) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? own[i] : acc[i] + own[i];
