@@ -46,7 +46,8 @@ Also printed (same JSON line):
   modes         the same call with feedback off, with fp32 output, with
                 the two-timescale compensator fused into push and reduce
                 (B then counts 16 bytes of state traffic instead of 8), and
-                with the other code width (8-bit codes: k_b = 1.03125).
+                with the other code width (8-bit codes: k_b = 1.03125), each
+                in the headline's schedule and back to back (`serial`).
   tp_block      one rank's row-parallel matmul with the entry pass fused in
                 its epilogue (echo_gemm_quantize_ef) against hipBLASLt +
                 echo_quantize_ef, at the Llama-3-8B down projection (TP = 4),
@@ -566,7 +567,14 @@ def main():
                 (f"bits{other_bits}", ef, out_bf16, 1.0, 0.0, other_bits)):
             rm = run_case(echo, torch, inputs, a.P, N_1GIB, m_bits, a.tiles, a.streams, max(5, a.steps // 3),
                           a.warmup, m_bf16, m_ef, time_kernel=False, alpha=alpha, beta=beta)
-            modes[name] = leg(rm)
+            extra = {"tiles": a.tiles, "streams": a.streams, "schedule": schedule_name(a.tiles, a.streams)}
+            if not a.no_serial and (a.tiles, a.streams) != (1, 1):
+                # the same mode back to back: with feedback off every stage is
+                # short, and the staged pipeline's launch and event costs weigh more
+                rms = run_case(echo, torch, inputs, a.P, N_1GIB, m_bits, 1, 1, max(5, a.steps // 3), a.warmup,
+                               m_bf16, m_ef, time_kernel=False, alpha=alpha, beta=beta)
+                extra["serial"] = leg(rms, {"tiles": 1, "streams": 1, "schedule": schedule_name(1, 1)})
+            modes[name] = leg(rm, extra)
     p8 = None
     if not a.no_p8 and a.P != 8:
         r8 = run_case(echo, torch, inputs, 8, N_1GIB, a.bits, a.tiles, a.streams, max(5, a.steps // 2),
