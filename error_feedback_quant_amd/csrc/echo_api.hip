@@ -36,6 +36,8 @@ constexpr size_t kReduceCompLds = 32 * 1024;
 constexpr int64_t kMaxTiles = 4096;
 // below this many push blocks per rank launch, one launch serves all ranks
 constexpr int64_t kBatchBelowBlocks = 4096;
+// one-tile calls of at most this many elements per rank run as one launch (onepass_kernel)
+constexpr int64_t kOnePassMaxElems = int64_t(1) << 20;
 
 int hip_fail(hipError_t e)
 {
@@ -231,6 +233,37 @@ int launch_gather(const echo::GatherArgs& a, int P, int slots, int bits, int gro
         if (group == 128) { if (bf) gather_go<8, true, 128>(a, grid, st); else gather_go<8, false, 128>(a, grid, st); }
         else { if (bf) gather_go<8, true, 256>(a, grid, st); else gather_go<8, false, 256>(a, grid, st); }
     }
+    return check_launch();
+}
+
+template <int B, int Q, int G, bool UP, bool BF>
+void onepass_go(const echo::OnePassArgs& a, dim3 grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((echo::onepass_kernel<B, Q, G, UP, BF>), grid, dim3(echo::kBlock), 0, st, a);
+}
+
+// the whole call in one launch: a.P * a.seg_waves wavefronts
+int launch_onepass(const echo::OnePassArgs& a, int bits, int group, int quant, bool upd, bool bf16, hipStream_t st)
+{
+    constexpr uint64_t kWaves = echo::kBlock / 64;
+    const uint64_t waves = (uint64_t)a.P * a.seg_waves;
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+#define ECHO_O4(B, Q, G, UP) \
+    if (bf16) onepass_go<B, Q, G, UP, true>(a, grid, st); else onepass_go<B, Q, G, UP, false>(a, grid, st);
+#define ECHO_O3(B, Q, G) \
+    if (upd) { ECHO_O4(B, Q, G, true) } else { ECHO_O4(B, Q, G, false) }
+#define ECHO_O2(B, Q) \
+    if (group == 128) { ECHO_O3(B, Q, 128) } else { ECHO_O3(B, Q, 256) }
+#define ECHO_O1(B)                                                          \
+    if (quant == echo::kNaive) { ECHO_O2(B, echo::kNaive) }                 \
+    else if (quant == echo::kSymmetric) { ECHO_O2(B, echo::kSymmetric) }    \
+    else if (quant == echo::kMse) { ECHO_O2(B, echo::kMse) }                \
+    else { ECHO_O2(B, echo::kZeroAware) }
+    if (bits == 4) { ECHO_O1(4) } else { ECHO_O1(8) }
+#undef ECHO_O1
+#undef ECHO_O2
+#undef ECHO_O3
+#undef ECHO_O4
     return check_launch();
 }
 
@@ -574,6 +607,52 @@ int sim_impl(const echo_sim_args* a, void* const* streams, int nstreams, bool no
                       s_comp = stage_stream(3);
     const bool multi = nst > 1;
 
+    // feedback forms: classic fused (-e written into comp), two-timescale
+    // fused (comp and slow updated in the kernels), or unfused (e into err,
+    // then echo_compensate after the last reduce)
+    const bool two_fused = a->ef && fused && a->beta > 0.0f;
+    const int flags = ((fused && !two_fused) ? ECHO_ERR_NEGATED : 0) | a->quant;
+    const echo::UpdArgs upd = make_upd(a->alpha, a->beta);
+    // Small tiles: one launch per stage serves every rank (the per-rank
+    // launches would be too small to fill the GPU, and the call is bound by
+    // launch latency).  Large tiles: one launch per rank, which measured
+    // faster than one launch over all ranks.
+    const bool batch = (int64_t)blocks_for((uint32_t)(tile_len / echo::kRow), kUPush) * (P - 1) < kBatchBelowBlocks;
+    const int per_launch = batch ? P : 1;
+    auto comp_of = [&](int r) -> float* { return a->ef ? a->comp[r] : nullptr; };
+    auto err_of = [&](int r) -> float* {
+        return (a->ef && !two_fused) ? (fused ? a->comp[r] : a->err[r]) : nullptr;
+    };
+    auto slow_of = [&](int r) -> float* { return two_fused ? a->slow[r] : nullptr; };
+
+    // A small message asked for in one tile: the whole call in one launch on
+    // the first stream (the stages work group by group, so no stage waits for
+    // another launch), then the separate update pass if the feedback is
+    // unfused.  More tiles keep the staged schedule the caller asked for.
+    if (a->tiles == 1 && n <= kOnePassMaxElems) {
+        echo::OnePassArgs oa;
+        std::memset(&oa, 0, sizeof(oa));
+        for (int r = 0; r < P; ++r) {
+            oa.x[r] = a->x[r]; oa.comp[r] = comp_of(r); oa.err[r] = err_of(r); oa.slow[r] = slow_of(r);
+            oa.out[r] = a->out[r]; oa.pc[r] = (uint8_t*)pc[r]; oa.pp[r] = (uint32_t*)pp[r];
+        }
+        oa.sc = sc; oa.sp = (uint32_t*)sp;
+        oa.upd = upd;
+        oa.S = S;
+        oa.seg_waves = (uint32_t)((S + echo::kWaveElems - 1) / echo::kWaveElems);
+        oa.P = P;
+        oa.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
+        rc = launch_onepass(oa, a->bits, a->group, quant_of(flags), two_fused, a->out_dtype == ECHO_OUT_BF16, st_main);
+        if (rc) return rc;
+        if (a->ef && !fused) {
+            for (int r = 0; r < P; ++r) {
+                rc = launch_compensate(a->err[r], a->comp[r], a->slow[r], n, a->alpha, a->beta, st_main);
+                if (rc) return rc;
+            }
+        }
+        return ECHO_OK;
+    }
+
     // events: start, per tile push-done and reduce-done, per stream done
     hipEvent_t* ev = nullptr;
     if (multi) {
@@ -593,24 +672,6 @@ int sim_impl(const echo_sim_args* a, void* const* streams, int nstreams, bool no
             if (used[k] != st_main && (he = hipStreamWaitEvent(used[k], ev_start, 0)) != hipSuccess)
                 return hip_fail(he);
     }
-
-    // feedback forms: classic fused (-e written into comp), two-timescale
-    // fused (comp and slow updated in the kernels), or unfused (e into err,
-    // then echo_compensate after the last reduce)
-    const bool two_fused = a->ef && fused && a->beta > 0.0f;
-    const int flags = ((fused && !two_fused) ? ECHO_ERR_NEGATED : 0) | a->quant;
-    const echo::UpdArgs upd = make_upd(a->alpha, a->beta);
-    // Small tiles: one launch per stage serves every rank (the per-rank
-    // launches would be too small to fill the GPU, and the call is bound by
-    // launch latency).  Large tiles: one launch per rank, which measured
-    // faster than one launch over all ranks.
-    const bool batch = (int64_t)blocks_for((uint32_t)(tile_len / echo::kRow), kUPush) * (P - 1) < kBatchBelowBlocks;
-    const int per_launch = batch ? P : 1;
-    auto comp_of = [&](int r) -> float* { return a->ef ? a->comp[r] : nullptr; };
-    auto err_of = [&](int r) -> float* {
-        return (a->ef && !two_fused) ? (fused ? a->comp[r] : a->err[r]) : nullptr;
-    };
-    auto slow_of = [&](int r) -> float* { return two_fused ? a->slow[r] : nullptr; };
 
     // The tail of tile t is enqueued after the push of tile t + 1, so that the
     // reduce of a tile can run beside the next tile's push even when the tail

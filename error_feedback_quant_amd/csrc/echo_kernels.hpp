@@ -1018,4 +1018,182 @@ __global__ __launch_bounds__(kBlock) void compensate_kernel(const CompArgs a)
     }
 }
 
+// -------------------------------------------------------- one-pass call --
+// A whole call in one launch, for small messages, where a launch per stage
+// costs more than the stage's work (a single call of 64 x 1024 per rank is
+// bound by launch latency).  The stages work group by group, so each
+// wavefront takes 512 elements of one segment (four groups of 128, or two of
+// 256) through all of them in the call's order: every other rank's push of
+// those elements (codes and parameters into that rank's push buffer), the
+// owner's reduce (the peers' codes read back from their push buffers, the
+// fp32 sum in rank order, the sum quantized once), and every rank's tail
+// (each rank reads the sum codes back and decodes them into its output).
+// Every rank's reads and writes are its own, as in the per-stage kernels; a
+// workgroup barrier between stages makes one lane's stores (the group's
+// parameters) visible to the others.
+struct OnePassArgs {
+    const uint16_t* x[kMaxP];
+    float* comp[kMaxP];     // compensation (null with feedback off); UPD rewrites it
+    float* err[kMaxP];      // error output (comp itself when negate), or null
+    float* slow[kMaxP];     // slow memory, UPD only
+    void* out[kMaxP];
+    uint8_t* pc[kMaxP];     // each rank's push codes and parameters, message-shaped
+    uint32_t* pp[kMaxP];
+    uint8_t* sc;            // sum codes and parameters, message-shaped
+    uint32_t* sp;
+    UpdArgs upd;
+    int64_t S;
+    uint32_t seg_waves;     // wavefronts per segment: ceil(S / 512)
+    int P;
+    int negate;
+};
+
+constexpr uint32_t kWaveElems = 64 * kEPL;
+
+template <int BITS, int QUANT, int GROUP, bool UPD, bool OUT_BF16>
+__global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t gw = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const uint32_t seg = gw / a.seg_waves;
+    // wavefronts past the last segment (the grid's last block) take part in
+    // the barriers with every lane inactive
+    const int o = seg < (uint32_t)a.P ? (int)seg : 0;
+    const int64_t so = (int64_t)(gw - seg * a.seg_waves) * kWaveElems + lane * kEPL;
+    const bool active = seg < (uint32_t)a.P && so < a.S;
+    // an inactive lane reads the segment's last 8 elements; segments hold
+    // whole groups, so its group is inactive as a whole and stores nothing
+    const int64_t e0 = (int64_t)o * a.S + (active ? so : a.S - kEPL);
+
+    // one rank's inputs at this lane's 8 elements: x, and the compensation
+    // and slow memory when they are read
+    struct In {
+        u32x4 x;
+        f32x4 c0, c1, m0, m1;
+    };
+    auto load_in = [&](int r) {
+        In v;
+        v.x = *(const u32x4*)(a.x[r] + e0);
+        v.c0 = v.c1 = v.m0 = v.m1 = f32x4{};
+        if (a.comp[r]) { v.c0 = *(const f32x4*)(a.comp[r] + e0); v.c1 = *(const f32x4*)(a.comp[r] + e0 + 4); }
+        if (UPD) { v.m0 = *(const f32x4*)(a.slow[r] + e0); v.m1 = *(const f32x4*)(a.slow[r] + e0 + 4); }
+        return v;
+    };
+    auto to_u = [&](int r, const In& v, float* u, float* m) {
+        unpack_bf16x8(v.x, u);
+        if (a.comp[r]) {
+            u[0] += v.c0.x; u[1] += v.c0.y; u[2] += v.c0.z; u[3] += v.c0.w;
+            u[4] += v.c1.x; u[5] += v.c1.y; u[6] += v.c1.z; u[7] += v.c1.w;
+        }
+        m[0] = v.m0.x; m[1] = v.m0.y; m[2] = v.m0.z; m[3] = v.m0.w;
+        m[4] = v.m1.x; m[5] = v.m1.y; m[6] = v.m1.z; m[7] = v.m1.w;
+    };
+    // the error of rank r's quantization: the compensator's new state
+    // (UPD), or the error (negated for the next call's compensation)
+    auto finish = [&](int r, const float* q, const QParams& p, const float* u, const float* m) {
+        if (!active) return;
+        float e[8];
+        if (UPD) {
+            float cn[8], mn[8];
+            group_error(q, p, u, false, e);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) update1(a.upd, e[i], m[i], cn[i], mn[i]);
+            *(f32x4*)(a.comp[r] + e0) = f32x4{cn[0], cn[1], cn[2], cn[3]};
+            *(f32x4*)(a.comp[r] + e0 + 4) = f32x4{cn[4], cn[5], cn[6], cn[7]};
+            *(f32x4*)(a.slow[r] + e0) = f32x4{mn[0], mn[1], mn[2], mn[3]};
+            *(f32x4*)(a.slow[r] + e0 + 4) = f32x4{mn[4], mn[5], mn[6], mn[7]};
+        } else if (a.err[r]) {
+            group_error(q, p, u, a.negate != 0, e);
+            *(f32x4*)(a.err[r] + e0) = f32x4{e[0], e[1], e[2], e[3]};
+            *(f32x4*)(a.err[r] + e0 + 4) = f32x4{e[4], e[5], e[6], e[7]};
+        }
+    };
+
+    // push: every other rank quantizes its copy of segment o; the next
+    // rank's inputs are requested before this rank's results are stored
+    {
+        int j = (o == 0) ? 1 : 0;
+        In cur;
+        if (j < a.P) cur = load_in(j);
+        while (j < a.P) {
+            int jn = j + 1;
+            if (jn == o) ++jn;
+            In nxt;
+            if (jn < a.P) nxt = load_in(jn);
+            float u[8], m[8], q[8];
+            to_u(j, cur, u, m);
+            const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.pc[j], a.pp[j], q);
+            finish(j, q, p, u, m);
+            cur = nxt;
+            j = jn;
+        }
+    }
+    __syncthreads();
+
+    // owner reduce: fp32 sum in rank order, the owner's term unquantized;
+    // every peer's codes are requested before the sum starts
+    {
+        const In own_in = load_in(o);
+        Packed<BITS> pk[kMaxP];
+        uint32_t pw[kMaxP];
+#pragma unroll
+        for (int j = 0; j < kMaxP; ++j) {
+            if (j < a.P && j != o) {
+                pk[j].load(a.pc[j], e0);
+                pw[j] = a.pp[j][e0 / GROUP];
+            }
+        }
+        float own[8], m[8], acc[8], q[8];
+        to_u(o, own_in, own, m);
+#pragma unroll
+        for (int j = 0; j < kMaxP; ++j) {
+            if (j >= a.P) break;
+            if (j == o) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? own[i] : acc[i] + own[i];
+            } else {
+                float qj[8], t[8];
+                pk[j].unpack(qj);
+                decode8_q<QUANT>(qj, pw[j], t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? t[i] : acc[i] + t[i];
+            }
+        }
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(acc, active, lane, e0, a.sc, a.sp, q);
+        finish(o, q, p, acc, m);
+    }
+    __syncthreads();
+
+    // tail: every rank reads the sum codes (all reads issued before the
+    // first output is stored) and decodes them
+    Packed<BITS> sk[kMaxP];
+    uint32_t sw[kMaxP];
+#pragma unroll
+    for (int r = 0; r < kMaxP; ++r) {
+        if (r < a.P) {
+            sk[r].load(a.sc, e0);
+            sw[r] = a.sp[e0 / GROUP];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxP; ++r) {
+        if (r >= a.P) break;
+        float q[8], v[8];
+        sk[r].unpack(q);
+        decode8(q, sw[r], v);
+        if (!active) continue;
+        if (OUT_BF16) {
+            u32x4 w;
+            w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2));
+            w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2));
+            w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2));
+            w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2));
+            *(u32x4*)((uint16_t*)a.out[r] + e0) = w;
+        } else {
+            *(f32x4*)((float*)a.out[r] + e0) = f32x4{v[0], v[1], v[2], v[3]};
+            *(f32x4*)((float*)a.out[r] + e0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+    }
+}
+
 }  // namespace echo

@@ -271,6 +271,13 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
  * streams may be NULL (null stream only).  Results do not depend on tiles or
  * streams (bit for bit).
  *
+ * One tile and at most 2^20 elements per rank: the whole call is one launch
+ * on streams[0] (each wavefront takes its groups through every rank's push,
+ * the owner's reduce and every rank's tail; every stage still writes and
+ * reads its own buffers), followed by echo_compensate when err[r] are given.
+ * Such a call is bound by launch latency, and one launch instead of one per
+ * stage cuts it; the results are the same bit for bit.
+ *
  * Feedback (ef = 1): every rank's comp is added at the entry pass.  With
  * err[r] == NULL for every rank the update is fused into the push and reduce
  * kernels: they write -e straight into comp (alpha = 1, beta = 0, classic
