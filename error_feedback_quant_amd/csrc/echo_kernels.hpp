@@ -1113,12 +1113,12 @@ __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
     // rank's inputs are requested before this rank's results are stored
     {
         int j = (o == 0) ? 1 : 0;
-        In cur;
+        In cur = {};
         if (j < a.P) cur = load_in(j);
         while (j < a.P) {
             int jn = j + 1;
             if (jn == o) ++jn;
-            In nxt;
+            In nxt = cur;
             if (jn < a.P) nxt = load_in(jn);
             float u[8], m[8], q[8];
             to_u(j, cur, u, m);
