@@ -126,9 +126,10 @@ def test_onegb_sampled_parity_and_identities(echo, P):
 def test_onegb_full_parity(echo, P):
     """Every element of the 1 GiB message (2^29 bf16 per rank, Laplace(0,1)),
     P = 4 and P = 8, bit for bit against the oracle's whole call: all P bf16
-    outputs and all P compensations.  Two calls carry the feedback: the
-    first in the headline schedule (one tile per segment on one stream), the
-    second in the benchmark's staged schedule (4 tiles on 4 streams).  The oracle's call runs on the host
+    outputs and all P compensations.  Three calls carry the feedback: the
+    first back to back (one tile per segment on one stream), the second in
+    the benchmark's headline schedule (4 tiles staged on 2 streams), the
+    third on 4 streams.  The oracle's call runs on the host
     as independent calls on mini messages made of the same range of every
     segment, in threads (its chunked form is pinned to one whole call on the
     CPU)."""
@@ -141,7 +142,7 @@ def test_onegb_full_parity(echo, P):
     outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
     ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, 4), dtype=torch.uint8, device=DEV)
     c_host = [np.zeros(n, np.float32) for _ in range(P)]      # state before the call
-    for call, (tiles, nstreams) in enumerate([(1, 1), (4, 4)]):
+    for call, (tiles, nstreams) in enumerate([(1, 1), (4, 2), (4, 4)]):
         say("onegb full", P, "call", call, "generate")
         xs = [inputs.laplace(r + 16 * call, n, device=DEV) for r in range(P)]
         xh = [host_u16(x) for x in xs]
@@ -177,12 +178,15 @@ def test_onegb_full_parity(echo, P):
 @pytest.mark.parametrize("mode", ["ef_off", "f32_out", "two_timescale", "bits8", "naive", "symmetric", "g256",
                                   "mse"])
 def test_onegb_full_parity_modes(echo, mode):
-    """The benchmark's other legs at full size (1 GiB message, P = 4, one tile
-    on one stream): feedback off, fp32 output, the two-timescale compensator
-    (alpha = 0.5, beta = 0.25) fused into push and reduce, 8-bit codes, and
-    Table 8's naive-zero-point and symmetric-grid quantizers, groups of
-    256, and the full method with its zero point searched.  Two calls carry the state; every output, compensation and
-    slow-memory element matches the oracle's whole call bit for bit."""
+    """The benchmark's other legs at full size (1 GiB message, P = 4):
+    feedback off, fp32 output, the two-timescale compensator (alpha = 0.5,
+    beta = 0.25) fused into push and reduce, 8-bit codes, and Table 8's
+    naive-zero-point and symmetric-grid quantizers, groups of 256, and the
+    full method with its zero point searched.  Two calls carry the state, the
+    first back to back (one tile on one stream), the second in the
+    benchmark's headline schedule (4 tiles staged on 2 streams); every output,
+    compensation and slow-memory element matches the oracle's whole call bit
+    for bit."""
     P, n = 4, 1 << 29
     L = 1 << 18
     ef = mode != "ef_off"
@@ -201,13 +205,14 @@ def test_onegb_full_parity_modes(echo, mode):
     ws = torch.empty(echo.echo_allreduce_sim_workspace_bytes(P, n, bits, group), dtype=torch.uint8, device=DEV)
     c_host = [np.zeros(n, np.float32) for _ in range(P)] if ef else None
     s_host = [np.zeros(n, np.float32) for _ in range(P)] if two else None
-    for call in range(2):
-        say("onegb mode", mode, "call", call)
+    for call, (tiles, nstreams) in enumerate([(1, 1), (4, 2)]):
+        say("onegb mode", mode, "call", call, "tiles", tiles, "streams", nstreams)
         xs = [inputs.laplace(r + 16 * call, n, device=DEV) for r in range(P)]
         xh = [host_u16(x) for x in xs]
-        a = echo.make_sim_args(xs, outs, ws, bits=bits, group=group, tiles=1, out_dtype=odt, ef=ef, alpha=alpha,
-                               beta=beta, comps=comps, slows=slows, quant=quant)
-        echo.echo_allreduce_sim(a)
+        streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+        a = echo.make_sim_args(xs, outs, ws, bits=bits, group=group, tiles=tiles, out_dtype=odt, ef=ef,
+                               alpha=alpha, beta=beta, comps=comps, slows=slows, quant=quant)
+        echo.echo_allreduce_sim(a, streams=streams)
         torch.cuda.synchronize()
         out_h = [host_f32(o) if odt == oracle.OUT_F32 else host_u16(o) for o in outs]
         c_after = [host_f32(c) for c in comps] if ef else None
