@@ -1165,7 +1165,9 @@ __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
     __syncthreads();
 
     // tail: every rank reads the sum codes (all reads issued before the
-    // first output is stored) and decodes them
+    // first output is stored) and decodes them.  The reads are identical, so
+    // a compiler memory barrier after each keeps them from being merged into
+    // one: each rank reads for itself, as in the per-stage tail.
     Packed<BITS> sk[kMaxP];
     uint32_t sw[kMaxP];
 #pragma unroll
@@ -1173,6 +1175,7 @@ __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
         if (r < a.P) {
             sk[r].load(a.sc, e0);
             sw[r] = a.sp[e0 / GROUP];
+            asm volatile("" ::: "memory");
         }
     }
 #pragma unroll
