@@ -6,9 +6,11 @@ owner's reduce and every rank's tail).  These cases cover it over the ranks,
 code widths, feedback forms, quantizers, group sizes and output types, on
 segments whose last wavefront is partly empty and grids whose last block
 holds wavefronts past the last segment, against the oracle's whole call over
-three calls that carry the state; the largest one-launch message and the
-smallest message above it against the oracle; and guard regions around
-every buffer the call writes."""
+three calls that carry the state; 16 seeded random cases (ranks, segment
+length up to the limit, width, quantizer, group size, feedback form, output
+type) over two calls; the largest one-launch message and the smallest
+message above it against the oracle; and guard regions around every buffer
+the call writes."""
 import numpy as np
 import pytest
 import torch
@@ -148,4 +150,29 @@ def test_one_launch_writes_nothing_outside_the_message(echo, ef_mode, odt):
     got = [[host_f32(o) if odt == oracle.OUT_F32 else host_u16(o) for o in outs]]
     gstate = dict(comps=[host_f32(c) for c in comps], slows=[host_f32(s) for s in slows] if slows else None,
                   errs=[host_f32(e) for e in errs] if errs else None)
+    check(got, gstate, want, wstate, P, odt)
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 9))
+    group = int(rng.choice([128, 256]))
+    # segments from one group up to the one-launch limit
+    max_gps = ONEPASS_MAX // (P * group)
+    gps = int(rng.choice([1, 2, 3, int(rng.integers(4, 80)), int(rng.integers(80, max_gps + 1))]))
+    bits = int(rng.choice([4, 8]))
+    quant = str(rng.choice(["zero_aware", "naive", "symmetric", "mse"]))
+    ef_mode = str(rng.choice(list(MODES)))
+    odt = int(rng.choice([oracle.OUT_F32, oracle.OUT_BF16]))
+    return P, group, gps, bits, quant, ef_mode, odt
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_one_launch_random_cases(echo, seed):
+    P, group, gps, bits, quant, ef_mode, odt = _random_case(20261203 + seed)
+    n = P * group * gps
+    say("one launch random", seed, P, group, gps, bits, quant, ef_mode, odt)
+    xs_list = [[rand_bf16(n, 50000 + 100 * seed + 10 * c + r, scale=0.5 + c) for r in range(P)] for c in range(2)]
+    got, gstate = run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, 1, 1, quant, group)
+    want, wstate = run_oracle_calls(xs_list, P, n, bits, ef_mode, odt, quant, group)
     check(got, gstate, want, wstate, P, odt)
