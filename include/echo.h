@@ -227,11 +227,12 @@ int echo_compensate(const float* err, float* comp_next, float* slow, int64_t n,
  * separate GEMM only up to fp32 rounding of the sum; everything after x is
  * bit-exact.
  * Performance: measured at a Llama-3-8B MLP down projection at TP = 4
- * (M = N = 4096, K = 3584), this call is currently slower than a library
- * matmul (hipBLASLt) followed by echo_quantize_ef, by roughly 5 to 10 %: its
- * matmul core is slower than the library's, and its epilogue (the push)
- * cannot overlap the matrix cores when every CU holds one output tile.
- * Prefer the separate pair where speed matters.
+ * (M = N = 4096, K = 3584), this call is usually slower than a library
+ * matmul (hipBLASLt) followed by echo_quantize_ef, by about 3 to 10 %
+ * depending on the GPU (on one it was 3 % faster): its matmul core is
+ * slower than the library's, and its epilogue (the push) cannot overlap the
+ * matrix cores when every CU holds one output tile.  Prefer the separate
+ * pair where speed matters.
  *
  *   a_bf16 (device, in)   bfloat16 bits [M][K], row-major (K contiguous)
  *   w_bf16 (device, in)   bfloat16 bits [N][K], row-major (K contiguous): the
