@@ -2,8 +2,10 @@
 echo_allreduce_sim for callers that cannot allocate device memory: through the
 C ABI, its outputs and compensation equal those of echo_allreduce_sim (bit for
 bit) on two calls in a row, the second with a smaller message (the static
-scratch keeps the first call's contents), with tiles; and a message whose
-workspace exceeds the static scratch is rejected with nothing enqueued."""
+scratch keeps the first call's contents), with tiles; a message whose
+workspace exceeds the static scratch is rejected with nothing enqueued; and
+the call captured in a HIP graph (what callers that cannot allocate often
+are) replays bit for bit like the eager call."""
 import numpy as np
 import pytest
 import torch
@@ -72,3 +74,54 @@ def test_noalloc_rejects_a_message_beyond_the_scratch(echo):
     torch.cuda.synchronize()
     for o in outs:
         assert bool((o == 0x3F3F).all())           # nothing was enqueued
+
+
+@pytest.mark.parametrize("tiles", [1, 3])
+def test_noalloc_call_captured_in_a_graph(echo, tiles):
+    """One call captured in a graph (torch.cuda.graph, on its capture stream)
+    and replayed three times, with eager work and synchronizations between the
+    replays: every replay gives what the same call gives eagerly, bit for bit,
+    with the compensation carried from replay to replay.  The call records one
+    launch (one tile) or its stages on one stream (three tiles): no memset and
+    no event.  The scratch's device address was looked up by an earlier,
+    eager call."""
+    P, n, bits = 4, 64 * 1024, 4
+    xs = [dev_u16(rand_bf16(n, 300 + r)) for r in range(P)]
+
+    def fresh():
+        comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+        outs = [torch.full((n,), 0x3F3F, dtype=torch.int16, device=DEV) for _ in range(P)]
+        a = echo.make_sim_args(xs, outs, None, bits=bits, tiles=tiles, out_dtype=echo.OUT_BF16, ef=True,
+                               comps=comps, workspace_bytes=0)
+        return a, comps, outs
+
+    say("noalloc graph", "tiles", tiles, "eager")
+    a_e, comps_e, outs_e = fresh()
+    want = []
+    for _ in range(3):
+        echo.echo_allreduce_sim_noalloc(a_e)
+        torch.cuda.synchronize()
+        want.append(([host_u16(o) for o in outs_e], [host_f32(c) for c in comps_e]))
+
+    say("noalloc graph", "tiles", tiles, "capture")
+    a, comps, outs = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        echo.echo_allreduce_sim_noalloc(a)
+    torch.cuda.synchronize()
+    # capturing ran nothing
+    for c in comps:
+        assert bool((c == 0).all())
+    for k in range(3):
+        say("noalloc graph", "tiles", tiles, "replay", k)
+        g.replay()
+        torch.cuda.synchronize()
+        got_outs, got_comps = [host_u16(o) for o in outs], [host_f32(c) for c in comps]
+        for r in range(P):
+            assert_bits_equal(got_outs[r], want[k][0][r], f"replay {k} out rank {r}")
+            assert_bits_equal(got_comps[r], want[k][1][r], f"replay {k} comp rank {r}")
+        # the program's own eager work between replays
+        junk = torch.randn(1 << 20, device=DEV)
+        float(junk.sum())
+        torch.cuda.synchronize()
+    del g
