@@ -14,8 +14,9 @@ side of the zero-point add, range not widened to 0, 2^b levels instead of
 2^b - 1, codes measured from the range start), in the zero-point search
 (tie rule, objective without the rounding part), in the call structure (wrong
 segment pushed, owner's term or compensation dropped or taken from a peer,
-summation order), in the compensator (sign, slow-memory input), in decoding
-and packing (off-by-one, nibble order, neighbouring group's parameters), in
+summation order), in the compensator (sign, slow-memory input, release
+taken from the updated memory or at rate 1 - beta), in decoding and packing
+(off-by-one, nibble order, neighbouring group's parameters), in
 the error's sign, and in the number formats (binary16 and bfloat16 ties,
 missing scale clamp).
 """
@@ -86,6 +87,20 @@ MUTATIONS = [
      [AR + "test_compensator_conserves_the_error_debt"]),
     ("slow memory fed alpha*e instead of (1 - alpha)*e",
      [("float m2 = oma * e;", "float m2 = alpha * e;", 0)],
+     [AR + "test_compensator_conserves_the_error_debt"]),
+    ("compensation computed from the already updated slow memory",
+     [("""            float b = beta * M;
+            comp_next[i] = -(a + b);
+            float m1 = omb * M;
+            float m2 = oma * e;
+            slow[i] = m1 + m2;""", """            float m1 = omb * M;
+            float m2 = oma * e;
+            slow[i] = m1 + m2;
+            float b = beta * slow[i];
+            comp_next[i] = -(a + b);""", 0)],
+     [AR + "test_compensator_conserves_the_error_debt"]),
+    ("slow memory released at rate 1 - beta instead of beta",
+     [("float b = beta * M;", "float b = omb * M;", 0)],
      [AR + "test_compensator_conserves_the_error_debt"]),
     ("decoder off by one code",
      [("float d = (float)q - echo_ref_f16_to_f32(zero_h);", "float d = (float)(q + 1) - echo_ref_f16_to_f32(zero_h);", 0)],
