@@ -11,8 +11,10 @@ The mistakes are the ones a reader of the Echo paper card (Table 8, Fig. 2(a),
 appendix Fig. 4) and of the PhantomByte article ("The cancellation rule")
 could plausibly make when writing the oracle: in the quantizer (tie rule,
 side of the zero-point add, range not widened to 0, 2^b levels instead of
-2^b - 1, codes measured from the range start), in the zero-point search
-(tie rule, objective without the rounding part), in the call structure (wrong
+2^b - 1, codes measured from the range start), in the ablations (the naive
+range widened to 0, the symmetric grid over all 2^b - 1 steps), in the
+zero-point search (tie rule, objective without the rounding part, the last
+zero point skipped), in the call structure (wrong
 segment pushed, owner's term or compensation dropped or taken from a peer,
 summation order), in the compensator (sign, slow-memory input, release
 taken from the updated memory or at rate 1 - beta), in decoding and packing
@@ -127,6 +129,17 @@ MUTATIONS = [
      ["tests/test_oracle_quantizer_mse.py::test_hand_worked_tie_takes_the_smaller_zero_point"]),
     ("zero-point search scores the clamped codes without the rounding part",
      [("d += (c - r) * (c + r - 2.0 * (double)t);", "d += (c - r) * (c - r);", 0)],
+     ["tests/test_oracle_quantizer_mse.py::test_exhaustive_exact_search_on_tiny_groups"]),
+    ("naive zero point with the range widened to contain 0",
+     [("float lo = v[0], hi = v[0];", "float lo = fminf(v[0], 0.0f), hi = fmaxf(v[0], 0.0f);", 0)],
+     ["tests/test_oracle_quantizer_variants.py::test_brute_force_one_decimal_lattice",
+      "tests/test_oracle_quantizer_variants.py::test_brute_force_random_magnitudes"]),
+    ("symmetric grid scaled over 2^b - 1 levels instead of 2^(b-1) - 1",
+     [("scale_bits(a / (float)Qh)", "scale_bits(a / (float)Qm)", 0)],
+     ["tests/test_oracle_quantizer_variants.py::test_brute_force_one_decimal_lattice",
+      "tests/test_oracle_quantizer_variants.py::test_symmetric_round_trip_and_zero"]),
+    ("zero-point search stopping one short of Qm",
+     [("for (int z = 0; z <= Qm; ++z) {", "for (int z = 0; z < Qm; ++z) {", 0)],
      ["tests/test_oracle_quantizer_mse.py::test_exhaustive_exact_search_on_tiny_groups"]),
     ("zero binary16 scale not clamped to 2^-24",
      [("if (sh == 0x0000u) sh = 0x0001u;", "if (0) sh = 0x0001u;", 0)],
