@@ -1,5 +1,6 @@
 // echo_api.hip — host side of libecho: argument checks, kernel launches and
-// the tile-staged multi-stream schedule of one simulated all-reduce call.
+// the tile-staged multi-stream schedule of one simulated all-reduce call (a
+// small call asked for in one tile runs as a single launch instead).
 //
 // The calls follow the problem statement of "Echo: Error-Compensated 4-Bit
 // Tensor-Parallel Communication for LLM Training and Inference" (arXiv
