@@ -28,6 +28,12 @@ def sources():
     return [os.path.join(CSRC, "echo_api.hip")]
 
 
+# test-only device code: the kernels' helpers evaluated on their own, built
+# with the library's flags (loaded by tests/test_gpu_*.py only)
+CHECK_SRC = os.path.join(ROOT, "tests", "c", "recip_scale_check.hip")
+CHECK_LIB = os.path.join(ROOT, "tests", "c", "librecip_scale_check.so")
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *sources(), "-o", tmp]
@@ -43,7 +49,22 @@ def build(verbose: bool = False) -> str:
     if msgs and verbose:
         sys.stderr.write("\n".join(msgs) + "\n")
     os.replace(tmp, LIB)
+    build_check(verbose)
     return LIB
+
+
+def build_check(verbose: bool = False) -> str:
+    tmp = CHECK_LIB + ".tmp"
+    cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, CHECK_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [l for l in (r.stderr or "").splitlines() if "is not a recognized feature for this target" not in l]
+    if r.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {CHECK_LIB}")
+    os.replace(tmp, CHECK_LIB)
+    return CHECK_LIB
 
 
 if __name__ == "__main__":

@@ -93,9 +93,10 @@ __device__ __forceinline__ void wave_lds_fence()
 
 // A value moved across lanes by DPP is an integer to the compiler; a float
 // min/max of it first re-canonicalizes it (one more instruction per step).
-// The group reduction therefore works on integer keys with the order of the
-// floats (finite values; -0 sorts below +0), and the move folds into
-// v_min_i32_dpp / v_max_i32_dpp.  The key map is its own inverse.
+// The group reduction therefore works on integers, and the move folds into
+// the integer min/max: on keys with the order of the floats (finite values;
+// -0 sorts below +0) for an arbitrary range, or on the raw patterns where
+// the range holds 0 (group_minmax).  The key map is its own inverse.
 __device__ __forceinline__ int order_key(float f)
 {
     const int b = __builtin_bit_cast(int, f);
@@ -119,22 +120,36 @@ __device__ __forceinline__ int dpp_i(int v)
 // min and max over the lanes of a group (16 lanes, or 32 for GROUP = 256);
 // every lane ends with the result.  Only the sign of a zero result can differ
 // from a sequential min/max, and no quantizer's output depends on it.
-template <int GROUP>
+//
+// Where the range holds 0 (zero-aware and MSE: every lane's lo <= 0 <= hi)
+// the raw bit patterns already sort and the key map is skipped: a lo is a
+// zero or a negative float, whose pattern read as an unsigned integer grows
+// with its magnitude (+0 is the smallest), so the smallest lo is the largest
+// unsigned pattern; a hi is a zero or a positive float, and those order as
+// signed integers (-0 is the smallest).  The symmetric grid reduces only hi
+// (max |v|, never negative); the naive range is any pair of floats.
+template <int GROUP, int QUANT>
 __device__ __forceinline__ void group_minmax(float& lo, float& hi)
 {
-    int l = order_key(lo), h = order_key(hi);
-    l = min(l, dpp_i<0xB1>(l));  h = max(h, dpp_i<0xB1>(h));    // quad_perm [1,0,3,2]
-    l = min(l, dpp_i<0x4E>(l));  h = max(h, dpp_i<0x4E>(h));    // quad_perm [2,3,0,1]
-    l = min(l, dpp_i<0x124>(l)); h = max(h, dpp_i<0x124>(h));   // row_ror:4
-    l = min(l, dpp_i<0x128>(l)); h = max(h, dpp_i<0x128>(h));   // row_ror:8
+    constexpr bool kRaw = QUANT != kNaive;
+    constexpr bool kLo = QUANT != kSymmetric;
+    int l = kRaw ? __builtin_bit_cast(int, lo) : order_key(lo);
+    int h = kRaw ? __builtin_bit_cast(int, hi) : order_key(hi);
+    auto take = [&](int ol, int oh) {
+        if constexpr (kLo) l = kRaw ? (int)max((uint32_t)l, (uint32_t)ol) : min(l, ol);
+        h = max(h, oh);
+    };
+    take(kLo ? dpp_i<0xB1>(l) : 0, dpp_i<0xB1>(h));     // quad_perm [1,0,3,2]
+    take(kLo ? dpp_i<0x4E>(l) : 0, dpp_i<0x4E>(h));     // quad_perm [2,3,0,1]
+    take(kLo ? dpp_i<0x124>(l) : 0, dpp_i<0x124>(h));   // row_ror:4
+    take(kLo ? dpp_i<0x128>(l) : 0, dpp_i<0x128>(h));   // row_ror:8
     if constexpr (GROUP == 256) {
         // rows 0<->1 and 2<->3: ds_swizzle in swap-16 mode hands every lane
         // the value of lane ^ 16 (through the LDS crossbar, no LDS memory)
-        l = min(l, __builtin_amdgcn_ds_swizzle(l, 0x401F));
-        h = max(h, __builtin_amdgcn_ds_swizzle(h, 0x401F));
+        take(kLo ? __builtin_amdgcn_ds_swizzle(l, 0x401F) : 0, __builtin_amdgcn_ds_swizzle(h, 0x401F));
     }
-    lo = from_order_key(l);
-    hi = from_order_key(h);
+    lo = kRaw ? __builtin_bit_cast(float, l) : from_order_key(l);
+    hi = kRaw ? __builtin_bit_cast(float, h) : from_order_key(h);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -226,6 +241,23 @@ __device__ __forceinline__ float div_by_const(float x)
     return as_f32(__builtin_fmaf(r, kInv, q0));
 }
 
+// 1/s, correctly rounded, for a binary16 scale s (2^-24 <= s <= 65504): one
+// Newton step from the hardware reciprocal r0 (within one ulp of 1/s).  With
+// s = M 2^k, M an integer below 2^11, the product s r0 has at most 35
+// significant bits, so e = 1 - s r0 (|e| <= 2^-23) is exact; r0 + r0 e is
+// (1 - e^2)/s, within 2^-46 of 1/s relative.  Unless M is a power of two,
+// 1/s lies at least 2^-36 (relative) from every midpoint between fp32
+// values (2^24 - (2t + 1) M 2^j is a nonzero integer), so the fma's one
+// rounding gives RN(1/s); for M a power of two 1/s is a float and 2^-46 is
+// far inside its rounding interval.  Three instructions instead of the
+// division's eleven.
+__device__ __forceinline__ float recip_scale(float s)
+{
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, r0, 1.0f);
+    return __builtin_fmaf(r0, e, r0);
+}
+
 template <int BITS, int QUANT>
 __device__ __forceinline__ QParams make_params(float lo, float hi)
 {
@@ -235,9 +267,9 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         // range holds 0; integer zero point, so 0 is exactly code z
         const uint32_t sb = scale_bits(div_by_const<(1 << BITS) - 1>(hi - lo));
         const float s = f16_bits_to_f32(sb);
-        const float inv = 1.0f / s;
+        const float inv = recip_scale(s);
         const float zr = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * inv), 0.0f, kQm);
-        const float zf = (float)(uint32_t)zr;  // through an integer, so a -0 becomes +0
+        const float zf = zr + 0.0f;             // a -0 becomes +0
         const bool zero = (hi == lo);          // all-zero group
         p.s = zero ? 0.0f : s;
         p.inv = zero ? 0.0f : inv;
@@ -247,7 +279,7 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         // plain min/max range; real-valued zero point -lo/s in binary16
         const uint32_t sb = scale_bits(div_by_const<(1 << BITS) - 1>(hi - lo));
         const float s = f16_bits_to_f32(sb);
-        const float inv = 1.0f / s;
+        const float inv = recip_scale(s);
         // 0 - lo, not -lo: +0 for a zero minimum.  Pinned in a register, as
         // the backend otherwise turns (0 - lo) * inv into (-lo) * inv.
         const float nlo = as_f32(0.0f - lo);
@@ -263,7 +295,7 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         constexpr float kMid = (float)(1 << (BITS - 1));
         const uint32_t sb = scale_bits(div_by_const<(1 << (BITS - 1)) - 1>(hi));
         const float s = f16_bits_to_f32(sb);
-        const float inv = 1.0f / s;
+        const float inv = recip_scale(s);
         const bool zero = (hi == 0.0f);
         p.s = zero ? 0.0f : s;
         p.inv = zero ? 0.0f : inv;
@@ -488,7 +520,7 @@ __device__ __forceinline__ QParams quantize_group(const float* u, bool active, u
 {
     float lo, hi;
     lane_stats<QUANT>(u, lo, hi);
-    group_minmax<GROUP>(lo, hi);
+    group_minmax<GROUP, QUANT>(lo, hi);
     QParams p = make_params<BITS, QUANT>(lo, hi);
     if constexpr (QUANT == kMse) {
         if (p.s != 0.0f) {          // an all-zero group keeps z = 0
