@@ -316,6 +316,16 @@ __device__ __forceinline__ float quant1(float u, const QParams& p)
         return __builtin_amdgcn_fmed3f(__builtin_rintf(u * p.inv) + p.zf, 0.0f, kQm);
 }
 
+// Codes as binary16 values 1024 + q: v_perm_b32 puts two code bytes of b
+// (bytes 0, 1 with kPermLo, bytes 2, 3 with kPermHi) under the exponent
+// byte 0x64 of binary16 1024, one per 16-bit half.  A value is widened where
+// it is used, which folds into a v_fma_mix operand (see decode_peer).
+constexpr uint32_t kBias16 = 0x64646464u;
+constexpr uint32_t kPermLo = 0x04010400u;
+constexpr uint32_t kPermHi = 0x04030402u;
+__device__ __forceinline__ float half_lo(uint32_t h) { return f16_bits_to_f32(h & 0xFFFFu); }
+__device__ __forceinline__ float half_hi(uint32_t h) { return f16_bits_to_f32(h >> 16); }
+
 // the 8 codes of a lane, packed (4-bit: one dword, 8-bit: two dwords)
 template <int BITS>
 struct Packed;
@@ -362,6 +372,15 @@ struct Packed<4> {
             q[2 * i + 1] = (float)((od >> (8 * i)) & 0xFFu);
         }
     }
+    // 1024 + q of the 8 codes (even codes from the low nibbles, odd from the high)
+    __device__ __forceinline__ void biased(float* qb) const
+    {
+        const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+        const uint32_t e0 = __builtin_amdgcn_perm(kBias16, ev, kPermLo), e1 = __builtin_amdgcn_perm(kBias16, ev, kPermHi);
+        const uint32_t o0 = __builtin_amdgcn_perm(kBias16, od, kPermLo), o1 = __builtin_amdgcn_perm(kBias16, od, kPermHi);
+        qb[0] = half_lo(e0); qb[2] = half_hi(e0); qb[4] = half_lo(e1); qb[6] = half_hi(e1);
+        qb[1] = half_lo(o0); qb[3] = half_hi(o0); qb[5] = half_lo(o1); qb[7] = half_hi(o1);
+    }
 };
 template <>
 struct Packed<8> {
@@ -398,6 +417,17 @@ struct Packed<8> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[4 + i] = (float)((w.y >> (8 * i)) & 0xFFu);
     }
+    // 1024 + q of the 8 codes
+    __device__ __forceinline__ void biased(float* qb) const
+    {
+        const uint32_t h[4] = {__builtin_amdgcn_perm(kBias16, w.x, kPermLo), __builtin_amdgcn_perm(kBias16, w.x, kPermHi),
+                               __builtin_amdgcn_perm(kBias16, w.y, kPermLo), __builtin_amdgcn_perm(kBias16, w.y, kPermHi)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qb[2 * i] = half_lo(h[i]);
+            qb[2 * i + 1] = half_hi(h[i]);
+        }
+    }
 };
 
 // decode of one parameter word: v = (q - z) * s (the same for every quantizer)
@@ -409,23 +439,31 @@ __device__ __forceinline__ void decode8(const float* q, uint32_t word, float* v)
     for (int i = 0; i < 8; ++i) v[i] = (q[i] - zf) * s;
 }
 
-// The same decode where the zero point is an integer (zero-aware and
-// symmetric quantizers): z <= 255 and s is a binary16 value (11 significant
-// bits), so z*s, q*s and their difference (q - z)*s all fit in 19 bits and
-// are exact in fp32; one fma q*s + (-(z*s)) then rounds an exact,
-// representable value and gives the bits of the two-step form, +0 included
-// when q == z.  The naive quantizer's zero point carries a fraction, so
-// there q - z can round and only the two-step form is right.
-template <int QUANT>
-__device__ __forceinline__ void decode8_q(const float* q, uint32_t word, float* v)
+// The same decode of a peer's codes where the zero point is an integer
+// (zero-aware, symmetric and MSE quantizers), from the biased codes 1024 + q:
+// z <= 255 and s is a binary16 value (11 significant bits), so (1024 + z) s
+// and (1024 + q) s fit in 22 bits and (q - z) s in 19, all exact in fp32;
+// one fma (1024 + q) s + (-(1024 + z) s) then rounds an exact, representable
+// value and gives the bits of the two-step form, +0 included when q == z.
+// The naive quantizer's zero point carries a fraction, so there q - z can
+// round and only the two-step form is right.
+template <int BITS, int QUANT>
+__device__ __forceinline__ void decode_peer(const Packed<BITS>& pk, uint32_t word, float* v)
 {
     if constexpr (QUANT == kNaive) {
+        float q[8];
+        pk.unpack(q);
         decode8(q, word, v);
     } else {
+        float qb[8];
+        pk.biased(qb);
         const float s = f16_bits_to_f32(word & 0xFFFFu);
-        const float nzs = -(f16_bits_to_f32(word >> 16) * s);
+        // 1024 + z in binary16 (exact below 2048), then -(1024 + z) s; the
+        // fma with 0 keeps both operands in their binary16 registers
+        const _Float16 zb = __builtin_bit_cast(_Float16, (uint16_t)(word >> 16)) + (_Float16)1024.0f;
+        const float c = __builtin_fmaf(-(float)zb, s, 0.0f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(q[i], s, nzs);
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(qb[i], s, c);
     }
 }
 
@@ -891,9 +929,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BITS == 
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? own[i] : acc[i] + own[i];
             } else {
-                float q[8], t[8];
-                pk[k][j].unpack(q);
-                decode8_q<QUANT>(q, pw[k][j], t);
+                float t[8];
+                decode_peer<BITS, QUANT>(pk[k][j], pw[k][j], t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? t[i] : acc[i] + t[i];
             }
@@ -1184,9 +1221,8 @@ __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? own[i] : acc[i] + own[i];
             } else {
-                float qj[8], t[8];
-                pk[j].unpack(qj);
-                decode8_q<QUANT>(qj, pw[j], t);
+                float t[8];
+                decode_peer<BITS, QUANT>(pk[j], pw[j], t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = (j == 0) ? t[i] : acc[i] + t[i];
             }
