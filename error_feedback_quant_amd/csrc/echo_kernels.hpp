@@ -194,6 +194,9 @@ __device__ __forceinline__ uint32_t scale_bits(float s32)
 }
 
 // Group parameters (one binary16 scale and one binary16 zero point per group)
+// (For an all-zero group the zero-aware, MSE and symmetric quantizers keep
+// s = 2^-24 here while the word stores scale 0; the codes and errors are the
+// same either way.)
 struct QParams {
     float s;        // scale as fp32 (exact binary16 value)
     float inv;      // 1/s, correctly rounded
@@ -270,11 +273,14 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         const float inv = recip_scale(s);
         const float zr = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * inv), 0.0f, kQm);
         const float zf = zr + 0.0f;             // a -0 becomes +0
-        const bool zero = (hi == lo);          // all-zero group
-        p.s = zero ? 0.0f : s;
-        p.inv = zero ? 0.0f : inv;
-        p.zf = zero ? 0.0f : zf;
-        p.word = zero ? 0u : (sb | (f32_to_f16_bits(zf) << 16));
+        // An all-zero group (hi == lo, both zeros) stores the word 0.  Its
+        // quotient is +0 (div_by_const maps -0 to +0), so s is the clamped
+        // 2^-24, inv 2^24 and z 0: every code is 0 and every error +0, as
+        // with s = 0, and only the word needs the special case.
+        p.s = s;
+        p.inv = inv;
+        p.zf = zf;
+        p.word = (hi == lo) ? 0u : (sb | (f32_to_f16_bits(zf) << 16));
     } else if constexpr (QUANT == kNaive) {
         // plain min/max range; real-valued zero point -lo/s in binary16
         const uint32_t sb = scale_bits(div_by_const<(1 << BITS) - 1>(hi - lo));
@@ -296,11 +302,12 @@ __device__ __forceinline__ QParams make_params(float lo, float hi)
         const uint32_t sb = scale_bits(div_by_const<(1 << (BITS - 1)) - 1>(hi));
         const float s = f16_bits_to_f32(sb);
         const float inv = recip_scale(s);
-        const bool zero = (hi == 0.0f);
-        p.s = zero ? 0.0f : s;
-        p.inv = zero ? 0.0f : inv;
+        // an all-zero group (hi == 0) stores scale 0; with the clamped s =
+        // 2^-24 its codes are kMid and its errors +0, as with s = 0
+        p.s = s;
+        p.inv = inv;
         p.zf = kMid;
-        p.word = (zero ? 0u : sb) | (f32_to_f16_bits(kMid) << 16);
+        p.word = ((hi == 0.0f) ? 0u : sb) | (f32_to_f16_bits(kMid) << 16);
     }
     return p;
 }
@@ -561,7 +568,7 @@ __device__ __forceinline__ QParams quantize_group(const float* u, bool active, u
     group_minmax<GROUP, QUANT>(lo, hi);
     QParams p = make_params<BITS, QUANT>(lo, hi);
     if constexpr (QUANT == kMse) {
-        if (p.s != 0.0f) {          // an all-zero group keeps z = 0
+        if (p.word != 0u) {         // an all-zero group keeps z = 0 (word 0)
             p.zf = search_zero<BITS, GROUP>(u, p.inv, p.zf);
             p.word = (p.word & 0xFFFFu) | (f32_to_f16_bits(p.zf) << 16);
         }
