@@ -351,6 +351,71 @@ def test_quantizer_variant_edge_groups(echo, quant):
             assert_bits_equal(host_f32(ed), we, "edge err")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric", "mse"])
+def test_groups_zero_on_every_rank_through_every_step(echo, quant, bits):
+    """Groups that are zero on every rank (+0 and -0 mixed), and groups that
+    hold one constant on every rank, with no compensation: every push stores
+    scale 0 for a zero group, the owner reduce decodes those peers' words and
+    sums to an all-zero group, which it stores with scale 0 as well, and
+    the tail decodes it; mixed with ordinary groups, bit for bit against the
+    oracle at each step (the naive quantizer also stores a constant group
+    with scale 0; the symmetric grid keeps its fixed zero point in the word)."""
+    P = 4
+    n = P * G * 18
+    Sn = n // P
+    flag = echo.QUANTS[quant]
+    rng = np.random.default_rng(41 + bits)
+    xs = []
+    for r in range(P):
+        v = rng.standard_normal(n).astype(np.float32)
+        b = v.reshape(-1, G)
+        b[0::3] = 0.0                                      # zero on every rank
+        b[0::9, ::2] = -0.0                                # with negative zeros in some
+        b[1::6] = 0.75                                     # one constant on every rank
+        xs.append(oracle.f32_to_bf16_bits(v))
+    cb = oracle.code_bytes(n, bits)
+    ng = n // G
+    pc_h = [np.full(cb, 0x3C, np.uint8) for _ in range(P)]
+    pp_h = [np.full(2 * ng, 0x7777, np.uint16) for _ in range(P)]
+    pc_d = [dev_u8(a) for a in pc_h]
+    pp_d = [dev_u16(a) for a in pp_h]
+    say("zero groups push", quant, bits)
+    for r in range(P):
+        oracle.quantize_ef(xs[r], None, n, P, r, 0, Sn, bits, G, pc_h[r], pp_h[r], None, flag)
+        echo.echo_quantize_ef(dev_u16(xs[r]), None, n, P, r, 0, Sn, bits, G, pc_d[r], pp_d[r], None, flag)
+    torch.cuda.synchronize()
+    for r in range(P):
+        assert_bits_equal(host_u8(pc_d[r]), pc_h[r], f"push codes {r}")
+        assert_bits_equal(host_u16(pp_d[r]), pp_h[r], f"push params {r}")
+        pushed = np.concatenate([pp_h[r][2 * (s * Sn // G):2 * ((s + 1) * Sn // G)] for s in range(P) if s != r])
+        assert np.count_nonzero(pushed[0::2] == 0) >= 3 * (Sn // G) // 3       # scale 0: the zero groups
+    say("zero groups reduce", quant, bits)
+    sc_h = np.full(cb, 0x11, np.uint8)
+    sp_h = np.full(2 * ng, 0x2222, np.uint16)
+    sc_d, sp_d = dev_u8(sc_h), dev_u16(sp_h)
+    for o in range(P):
+        oracle.reduce_segment(xs[o], None, pc_h, pp_h, P, o, n, 0, Sn, bits, G, sc_h, sp_h, None, flag)
+        echo.echo_reduce_segment(dev_u16(xs[o]), None, [None if j == o else pc_d[j] for j in range(P)],
+                                 [None if j == o else pp_d[j] for j in range(P)], P, o, n, 0, Sn, bits, G,
+                                 sc_d, sp_d, None, flag)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u8(sc_d), sc_h, "sum codes")
+    assert_bits_equal(host_u16(sp_d), sp_h, "sum params")
+    assert np.count_nonzero(sp_h[0::2] == 0) >= ng // 3
+    for odt in (oracle.OUT_F32, oracle.OUT_BF16):
+        say("zero groups gather", quant, bits, odt)
+        if odt == oracle.OUT_F32:
+            want, out_d = sentinel_f32(n), dev_f32(sentinel_f32(n))
+        else:
+            want, out_d = np.full(n, 0xBEEF, np.uint16), dev_u16(np.full(n, 0xBEEF, np.uint16))
+        oracle.gather_dequant(sc_h, sp_h, n, 0, Sn, P, bits, G, want, odt)
+        echo.echo_gather_dequant(sc_d, sp_d, n, 0, Sn, P, bits, G, out_d, odt)
+        torch.cuda.synchronize()
+        got = host_f32(out_d) if odt == oracle.OUT_F32 else host_u16(out_d)
+        assert_bits_equal(got, want, "decoded output")
+
+
 def search_groups(bits, group, count, seed):
     """Groups whose searched zero point differs from the closed form (chosen
     by the oracle), mixed with groups where it does not: one-decimal values

@@ -176,3 +176,34 @@ def test_one_launch_random_cases(echo, seed):
     got, gstate = run_gpu_calls(echo, xs_list, P, n, bits, ef_mode, odt, 1, 1, quant, group)
     want, wstate = run_oracle_calls(xs_list, P, n, bits, ef_mode, odt, quant, group)
     check(got, gstate, want, wstate, P, odt)
+
+
+def _with_zero_groups(x, group):
+    """bf16 partials with every third group zero (some with -0) and every
+    sixth (offset 1) one constant, the same rows on every rank."""
+    b = np.frombuffer(x.tobytes(), np.uint16).copy().reshape(-1, group)
+    b[0::3] = 0x0000
+    b[0::9, ::2] = 0x8000                       # -0
+    b[1::6] = 0x3F40                            # 0.75
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("quant", ["zero_aware", "naive", "symmetric", "mse"])
+def test_one_launch_groups_zero_on_every_rank(echo, quant, bits):
+    """Zero (and, for the naive quantizer, constant) groups on every rank
+    through the one-launch call over three calls with classic feedback: the
+    pushes store scale 0 for them, the owner decodes those peers' words and
+    stores its all-zero sums with scale 0, and the compensation stays zero
+    there; bit for bit against the oracle."""
+    P, group, gps = 4, 128, 18
+    n = P * group * gps
+    xs_list = [[_with_zero_groups(rand_bf16(n, 9700 + 10 * c + r + bits), group) for r in range(P)]
+               for c in range(3)]
+    say("one launch zero groups", quant, bits)
+    got, gstate = run_gpu_calls(echo, xs_list, P, n, bits, "classic", oracle.OUT_BF16, 1, 1, quant, group)
+    want, wstate = run_oracle_calls(xs_list, P, n, bits, "classic", oracle.OUT_BF16, quant, group)
+    check(got, gstate, want, wstate, P, oracle.OUT_BF16)
+    zero_rows = np.arange(n // group)[0::3]
+    for r in range(P):
+        assert np.all(wstate["comps"][r].reshape(-1, group)[zero_rows] == 0)
