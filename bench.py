@@ -216,6 +216,41 @@ def leg(r, extra=None):
     return d
 
 
+def graph_call_latency(echo, torch, xs, calls=50, replays=7):
+    """Device-side time per call of a small workload: `calls` consecutive
+    calls of echo_allreduce_sim_noalloc (the allocation-free form; one tile,
+    so one launch each at this size) captured in one HIP graph and replayed,
+    so that no host work sits between the calls.  The compensation carries
+    from call to call as in eager use."""
+    dev = "cuda:0"
+    P, n = len(xs), xs[0].numel()
+    comps = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(P)]
+    outs = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(P)]
+    a = echo.make_sim_args(xs, outs, None, bits=4, tiles=1, out_dtype=echo.OUT_BF16, ef=True, comps=comps,
+                           workspace_bytes=0)
+    echo.echo_allreduce_sim_noalloc(a)    # an eager call first looks up the scratch's device address
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            echo.echo_allreduce_sim_noalloc(a)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    per_call = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        g.replay()
+        e1.record(main)
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) / calls)
+    del g
+    per_call.sort()
+    return {"calls_per_graph": calls, "replays": replays, "call_us_median": round(per_call[replays // 2] * 1e3, 2),
+            "call_us_min": round(per_call[0] * 1e3, 2),
+            "what": "calls captured in one HIP graph (echo_allreduce_sim_noalloc) and replayed: no host work between calls"}
+
+
 def config_legs(echo, torch, inputs):
     """Per-call throughput of the single-call, depth-chain, 8-bit-chain and
     training workloads (one call each, inputs of the workload's recipe),
@@ -227,7 +262,8 @@ def config_legs(echo, torch, inputs):
     n = xs[0].numel()
     r = run_case(echo, torch, inputs, P, n, 4, 1, 1, 200, 20, True, True, time_kernel=False, xs=xs)
     out["single_call_64x1024"] = leg(r, {"P": P, "n": n, "bits": 4, "ef": "classic", "cache_resident": True,
-                                         "latency_us_median": round(r["call_ms"]["median"] * 1e3, 1)})
+                                         "latency_us_median": round(r["call_ms"]["median"] * 1e3, 1),
+                                         "graph_replay": graph_call_latency(echo, torch, xs)})
     sigma = inputs.chain_channel_scale(device=dev)
     for ef in (True, False):
         xs = [inputs.chain(r, 0, sigma_h=sigma, device=dev) for r in range(P)]

@@ -243,12 +243,10 @@ void onepass_go(const echo::OnePassArgs& a, dim3 grid, hipStream_t st)
     hipLaunchKernelGGL((echo::onepass_kernel<B, Q, G, UP, BF>), grid, dim3(echo::kBlock), 0, st, a);
 }
 
-// the whole call in one launch: a.P * a.seg_waves wavefronts
+// the whole call in one launch: one block per 512-element chunk of every segment
 int launch_onepass(const echo::OnePassArgs& a, int bits, int group, int quant, bool upd, bool bf16, hipStream_t st)
 {
-    constexpr uint64_t kWaves = echo::kBlock / 64;
-    const uint64_t waves = (uint64_t)a.P * a.seg_waves;
-    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+    const dim3 grid((unsigned)((uint64_t)a.P * a.seg_chunks));
 #define ECHO_O4(B, Q, G, UP) \
     if (bf16) onepass_go<B, Q, G, UP, true>(a, grid, st); else onepass_go<B, Q, G, UP, false>(a, grid, st);
 #define ECHO_O3(B, Q, G) \
@@ -640,7 +638,7 @@ int sim_impl(const echo_sim_args* a, void* const* streams, int nstreams, bool no
         oa.sc = sc; oa.sp = (uint32_t*)sp;
         oa.upd = upd;
         oa.S = S;
-        oa.seg_waves = (uint32_t)((S + echo::kWaveElems - 1) / echo::kWaveElems);
+        oa.seg_chunks = (uint32_t)((S + echo::kChunkElems - 1) / echo::kChunkElems);
         oa.P = P;
         oa.negate = (flags & ECHO_ERR_NEGATED) ? 1 : 0;
         rc = launch_onepass(oa, a->bits, a->group, quant_of(flags), two_fused, a->out_dtype == ECHO_OUT_BF16, st_main);

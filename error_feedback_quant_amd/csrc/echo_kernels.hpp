@@ -1119,27 +1119,33 @@ struct OnePassArgs {
     uint32_t* sp;
     UpdArgs upd;
     int64_t S;
-    uint32_t seg_waves;     // wavefronts per segment: ceil(S / 512)
+    uint32_t seg_chunks;    // 512-element chunks per segment: ceil(S / 512)
     int P;
     int negate;
 };
 
-constexpr uint32_t kWaveElems = 64 * kEPL;
+constexpr uint32_t kChunkElems = 64 * kEPL;   // one wavefront's 512 elements
 
+// The whole call in one launch, for small messages.  Block b takes chunk
+// b mod seg_chunks of segment (owner) o = b / seg_chunks, and its four
+// wavefronts split the ranks: wavefront w serves ranks w and w + 4.  Each
+// wavefront pushes its ranks' copies of the chunk (every rank but the
+// owner), the owner's wavefront (o mod 4) reduces the chunk, and each
+// wavefront decodes the sum into its ranks' outputs.  Workgroup barriers
+// between the stages make the codes and parameters one wavefront stored
+// visible to the others.  Every rank still writes and reads its own buffers.
 template <int BITS, int QUANT, int GROUP, bool UPD, bool OUT_BF16>
 __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
 {
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t gw = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    const uint32_t seg = gw / a.seg_waves;
-    // wavefronts past the last segment (the grid's last block) take part in
-    // the barriers with every lane inactive
-    const int o = seg < (uint32_t)a.P ? (int)seg : 0;
-    const int64_t so = (int64_t)(gw - seg * a.seg_waves) * kWaveElems + lane * kEPL;
-    const bool active = seg < (uint32_t)a.P && so < a.S;
+    const int wave = (int)(threadIdx.x >> 6);
+    const int o = (int)(blockIdx.x / a.seg_chunks);          // the grid holds exactly P * seg_chunks blocks
+    const int64_t so = (int64_t)(blockIdx.x - (uint32_t)o * a.seg_chunks) * kChunkElems + lane * kEPL;
+    const bool active = so < a.S;
     // an inactive lane reads the segment's last 8 elements; segments hold
     // whole groups, so its group is inactive as a whole and stores nothing
     const int64_t e0 = (int64_t)o * a.S + (active ? so : a.S - kEPL);
+    const bool reducer = wave == (o & 3);
 
     // one rank's inputs at this lane's 8 elements: x, and the compensation
     // and slow memory when they are read
@@ -1185,31 +1191,32 @@ __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
         }
     };
 
-    // push: every other rank quantizes its copy of segment o; the next
-    // rank's inputs are requested before this rank's results are stored
-    {
-        int j = (o == 0) ? 1 : 0;
-        In cur = {};
-        if (j < a.P) cur = load_in(j);
-        while (j < a.P) {
-            int jn = j + 1;
-            if (jn == o) ++jn;
-            In nxt = cur;
-            if (jn < a.P) nxt = load_in(jn);
-            float u[8], m[8], q[8];
-            to_u(j, cur, u, m);
-            const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.pc[j], a.pp[j], q);
-            finish(j, q, p, u, m);
-            cur = nxt;
-            j = jn;
-        }
+    // push: this wavefront's ranks other than the owner quantize their copy
+    // of the chunk (both ranks' inputs requested first); the owner's
+    // wavefront also requests the owner's inputs for the reduce
+    const int r0 = wave, r1 = wave + 4;
+    const bool push0 = r0 < a.P && r0 != o, push1 = r1 < a.P && r1 != o;
+    In in0 = {}, in1 = {}, own_in = {};
+    if (push0) in0 = load_in(r0);
+    if (push1) in1 = load_in(r1);
+    if (reducer) own_in = load_in(o);
+    if (push0) {
+        float u[8], m[8], q[8];
+        to_u(r0, in0, u, m);
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.pc[r0], a.pp[r0], q);
+        finish(r0, q, p, u, m);
+    }
+    if (push1) {
+        float u[8], m[8], q[8];
+        to_u(r1, in1, u, m);
+        const QParams p = quantize_group<BITS, QUANT, GROUP>(u, active, lane, e0, a.pc[r1], a.pp[r1], q);
+        finish(r1, q, p, u, m);
     }
     __syncthreads();
 
     // owner reduce: fp32 sum in rank order, the owner's term unquantized;
     // every peer's codes are requested before the sum starts
-    {
-        const In own_in = load_in(o);
+    if (reducer) {
         Packed<BITS> pk[kMaxP];
         uint32_t pw[kMaxP];
 #pragma unroll
@@ -1239,26 +1246,28 @@ __global__ __launch_bounds__(kBlock) void onepass_kernel(const OnePassArgs a)
     }
     __syncthreads();
 
-    // tail: every rank reads the sum codes (all reads issued before the
-    // first output is stored) and decodes them.  The reads are identical, so
-    // a compiler memory barrier after each keeps them from being merged into
-    // one: each rank reads for itself, as in the per-stage tail.
-    Packed<BITS> sk[kMaxP];
-    uint32_t sw[kMaxP];
+    // tail: each of this wavefront's ranks reads the sum codes (both reads
+    // issued before the first output is stored) and decodes them.  The
+    // reads are identical, so a compiler memory barrier after each keeps
+    // them from being merged into one: each rank reads for itself, as in the
+    // per-stage tail.
+    Packed<BITS> sk[2];
+    uint32_t sw[2];
 #pragma unroll
-    for (int r = 0; r < kMaxP; ++r) {
-        if (r < a.P) {
-            sk[r].load(a.sc, e0);
-            sw[r] = a.sp[e0 / GROUP];
+    for (int k = 0; k < 2; ++k) {
+        if (wave + 4 * k < a.P) {
+            sk[k].load(a.sc, e0);
+            sw[k] = a.sp[e0 / GROUP];
             asm volatile("" ::: "memory");
         }
     }
 #pragma unroll
-    for (int r = 0; r < kMaxP; ++r) {
+    for (int k = 0; k < 2; ++k) {
+        const int r = wave + 4 * k;
         if (r >= a.P) break;
         float q[8], v[8];
-        sk[r].unpack(q);
-        decode8(q, sw[r], v);
+        sk[k].unpack(q);
+        decode8(q, sw[k], v);
         if (!active) continue;
         if (OUT_BF16) {
             u32x4 w;

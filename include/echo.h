@@ -273,9 +273,11 @@ int echo_gemm_quantize_ef(const uint16_t* a_bf16, const uint16_t* w_bf16, int64_
  * streams (bit for bit).
  *
  * One tile and at most 2^20 elements per rank: the whole call is one launch
- * on streams[0] (each wavefront takes its groups through every rank's push,
- * the owner's reduce and every rank's tail; every stage still writes and
- * reads its own buffers), followed by echo_compensate when err[r] are given.
+ * on streams[0] (each block takes one 512-element chunk of one segment, and
+ * its four wavefronts split the ranks: they push their ranks' copies, the
+ * owner's wavefront reduces, and each decodes the sum into its ranks'
+ * outputs; every stage still writes and reads its own buffers), followed by
+ * echo_compensate when err[r] are given.
  * Such a call is bound by launch latency, and one launch instead of one per
  * stage cuts it; the results are the same bit for bit.
  *

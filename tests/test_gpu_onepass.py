@@ -1,12 +1,13 @@
 """GPU parity of the one-launch form of echo_allreduce_sim.
 
 A call asked for in one tile with at most 2^20 elements per rank runs as one
-launch (each wavefront takes its groups through every rank's push, the
-owner's reduce and every rank's tail).  These cases cover it over the ranks,
-code widths, feedback forms, quantizers, group sizes and output types, on
-segments whose last wavefront is partly empty and grids whose last block
-holds wavefronts past the last segment, against the oracle's whole call over
-three calls that carry the state; 16 seeded random cases (ranks, segment
+launch (each block takes one 512-element chunk of one segment through every
+rank's push, the owner's reduce and every rank's tail, its four wavefronts
+splitting the ranks).  These cases cover it over the ranks (more than four,
+where a wavefront serves two), code widths, feedback forms, quantizers,
+group sizes and output types, on segments whose last chunk is partly empty
+(down to one group), against the oracle's whole call over three calls that
+carry the state; 16 seeded random cases (ranks, segment
 length up to the limit, width, quantizer, group size, feedback form, output
 type) over two calls; the largest one-launch message and the smallest
 message above it against the oracle; and guard regions around every buffer
@@ -46,13 +47,13 @@ CASES = [
     # P, bits, ef, out, quant, group, groups per segment
     (1, 4, "classic", oracle.OUT_BF16, "zero_aware", 128, 37),
     (2, 8, "off", oracle.OUT_F32, "zero_aware", 128, 37),
-    (3, 4, "two", oracle.OUT_F32, "zero_aware", 128, 37),          # 30 wavefronts: 2 past the last segment
+    (3, 4, "two", oracle.OUT_F32, "zero_aware", 128, 37),          # last chunk: one group
     (4, 4, "classic", oracle.OUT_BF16, "zero_aware", 128, 37),
     (4, 4, "classic_unfused", oracle.OUT_F32, "naive", 128, 37),
-    (4, 8, "two_fused", oracle.OUT_BF16, "symmetric", 128, 5),      # one partly empty wavefront per segment
+    (4, 8, "two_fused", oracle.OUT_BF16, "symmetric", 128, 5),      # one partly empty chunk per segment
     (4, 4, "classic", oracle.OUT_F32, "mse", 128, 37),
     (4, 4, "two_fused", oracle.OUT_F32, "zero_aware", 256, 19),
-    (5, 8, "classic", oracle.OUT_BF16, "naive", 256, 19),
+    (5, 8, "classic", oracle.OUT_BF16, "naive", 256, 19),           # wavefront 0 serves ranks 0 and 4
     (8, 4, "off", oracle.OUT_BF16, "zero_aware", 128, 37),
     (8, 8, "two", oracle.OUT_F32, "mse", 256, 3),
     (8, 4, "classic_unfused", oracle.OUT_BF16, "symmetric", 256, 1),  # one group of 256 per segment
