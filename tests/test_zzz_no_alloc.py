@@ -5,7 +5,7 @@ bit) on two calls in a row, the second with a smaller message (the static
 scratch keeps the first call's contents), with tiles; a message whose
 workspace exceeds the static scratch is rejected with nothing enqueued; and
 the call captured in a HIP graph (what callers that cannot allocate often
-are) replays bit for bit like the eager call."""
+are) replays bit for bit like the eager call, also five calls to a graph."""
 import numpy as np
 import pytest
 import torch
@@ -124,4 +124,46 @@ def test_noalloc_call_captured_in_a_graph(echo, tiles):
         junk = torch.randn(1 << 20, device=DEV)
         float(junk.sum())
         torch.cuda.synchronize()
+    del g
+
+
+@pytest.mark.parametrize("tiles", [1, 3])
+def test_noalloc_calls_captured_five_to_a_graph(echo, tiles):
+    """Five consecutive calls captured in one graph (as the benchmark's
+    device-time measurement captures fifty), the compensation carried from
+    call to call: the first replay equals five eager calls and the second
+    ten, bit for bit."""
+    P, n, bits, calls = 4, 64 * 1024, 4, 5
+    xs = [dev_u16(rand_bf16(n, 500 + r)) for r in range(P)]
+
+    def fresh():
+        comps = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(P)]
+        outs = [torch.full((n,), 0x3F3F, dtype=torch.int16, device=DEV) for _ in range(P)]
+        a = echo.make_sim_args(xs, outs, None, bits=bits, tiles=tiles, out_dtype=echo.OUT_BF16, ef=True,
+                               comps=comps, workspace_bytes=0)
+        return a, comps, outs
+
+    say("noalloc graph x5", "tiles", tiles, "eager")
+    a_e, comps_e, outs_e = fresh()
+    want = {}
+    for c in range(1, 2 * calls + 1):
+        echo.echo_allreduce_sim_noalloc(a_e)
+        torch.cuda.synchronize()
+        if c % calls == 0:
+            want[c] = ([host_u16(o) for o in outs_e], [host_f32(x) for x in comps_e])
+
+    say("noalloc graph x5", "tiles", tiles, "capture")
+    a, comps, outs = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            echo.echo_allreduce_sim_noalloc(a)
+    torch.cuda.synchronize()
+    for k in (1, 2):
+        say("noalloc graph x5", "tiles", tiles, "replay", k)
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(P):
+            assert_bits_equal(host_u16(outs[r]), want[k * calls][0][r], f"replay {k} out rank {r}")
+            assert_bits_equal(host_f32(comps[r]), want[k * calls][1][r], f"replay {k} comp rank {r}")
     del g
