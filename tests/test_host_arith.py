@@ -14,6 +14,13 @@ every r0 within two ulps of RN(1/s), that r1 is the IEEE quotient 1/s, and
 that the same step misses it for some full 24-bit divisors (the 11-bit
 significand is what makes it exact).  tests/test_gpu_recip_scale.py checks
 the kernels' own function on the GPU for every binary16 scale.
+
+The owner reduce decodes a peer's codes for an integer zero point as
+fma(binary16(1024 + q), s, fma(-(1024 + z), s, 0)).
+tests/c/biased_decode_check.c checks that this equals the two-step decode
+(q - z) * s bit for bit for every positive finite binary16 s and every q, z
+in [0, 255] (and s = 0 where q == z), and that a decode with two roundings
+does differ at full 24-bit scales.
 """
 import os
 import shutil
@@ -45,3 +52,13 @@ def test_newton_reciprocal_of_a_binary16_scale_is_correctly_rounded(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "checked=158715 mismatches=0 " in r.stdout, r.stdout
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_biased_code_decode_equals_the_two_step_decode(tmp_path):
+    exe = tmp_path / "biased_decode_check"
+    subprocess.run(["gcc", "-O3", "-march=native", "-fopenmp", "-ffp-contract=off", "-o", str(exe),
+                    os.path.join(HERE, "c", "biased_decode_check.c"), "-lm"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "checked=2080309504 mismatches=0 unbiased_fma_mismatches=0 " in r.stdout, r.stdout
